@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 block-scaled GEMM hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload I]
+
+A step is one GEMM call (dense or grouped) over one batch of seeded synthetic
+operands already resident in HBM.  W untimed warm-up steps are followed by
+exactly K timed steps, bracketed by torch.cuda.synchronize() on both sides.
+Operand copies are rotated so that the working set of consecutive steps
+exceeds the 256 MB Infinity Cache: every step reads its inputs from HBM.
+
+One JSON line is printed on stdout.  `value` is throughput over the timed
+region (TFLOP/s of algorithmic work = 2 * real_rows * N * K, or GB/s of
+algorithmic bytes for the memory-bound skinny shape).  `roofline.achieved`
+uses the kernel's average duration from HIP events recorded on the launch
+stream around every timed step.  `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload on this host.
+
+Workloads (seeded, synthetic; see inputs.make_config):
+  1  dense 256^3, FP32 out                      (parity case)
+  2  dense 4096^3, per-block magnitudes, BF16   (default)
+  3  skinny 64 x 12288 x 4096, outliers, BF16   (HBM-bound)
+  4  MoE 8 experts, N = K = 4096, top-2 uniform
+  5  MoE 64 experts, N = K = 2048, top-2 Zipf(1.1)
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 block-scaled GEMM TFLOPS (% of FP8 MFMA peak); HBM GB/s for M≤64"
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA (no sparsity)
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+INFINITY_CACHE = 256 << 20
+HBM_BOUND = {3, 5}           # workloads whose roofline is HBM bandwidth
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "moe_grouped_gemm_block_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    or None when it is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))[workload_name]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("kernel_hash") != kernel_source_hash():
+        return None
+    return int(rec["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(p, target_s: float = 12.0):
+    """Time the oracle (as it stands) on rows of the same workload."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d["num_threads"] for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    M = p.M
+    rng = np.random.default_rng(0)
+
+    def run(rows):
+        t = time.perf_counter()
+        if p.grouped:
+            oracle.grouped_gemm(p.A, p.sA, p.B, p.sB, p.group_offsets, rows=rows)
+        else:
+            oracle.gemm_blockscaled(p.A, p.sA, p.B, p.sB, rows=rows)
+        return time.perf_counter() - t
+
+    calib = np.sort(rng.choice(M, size=min(M, 64), replace=False))
+    dt = run(calib)
+    n = int(min(M, max(64, len(calib) * target_s / max(dt, 1e-6))))
+    rows = np.sort(rng.choice(M, size=n, replace=False)) if n < M else np.arange(M)
+    dt = run(rows)
+    flop = 2.0 * len(rows) * p.N * p.K
+    if p.grouped:
+        # pad rows cost the oracle as much as real ones; count only the real share
+        flop *= p.real_rows / p.M
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{len(rows)} of {M} output rows (all {p.N} columns, K={p.K}) of workload "
+                      f"{p.name}, float64 numpy/BLAS"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--rotate", type=int, default=0, help="operand copies (0 = enough to exceed the Infinity Cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this path has no multi-GPU sharding)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from moe_grouped_gemm_block_amd import dg
+    from moe_grouped_gemm_block_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dg.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.perf_counter()
+    p = I.make_config(args.workload)
+    log(f"generated {p.name} in {time.perf_counter() - t0:.1f}s: M={p.M} N={p.N} K={p.K} "
+        f"G={p.G} real_rows={p.real_rows}")
+
+    step_bytes = p.algorithmic_bytes()
+    R = args.rotate or max(1, -(-2 * INFINITY_CACHE // step_bytes))
+    cdt = torch.float32 if p.out_dtype == "f32" else torch.bfloat16
+    host = {k: torch.from_numpy(np.ascontiguousarray(v)) for k, v in
+            dict(A=p.A, sA=p.sA, B=p.B, sB=p.sB).items()}
+    if p.grouped:
+        host["offs"] = torch.from_numpy(p.group_offsets.astype(np.int32))
+    copies = []
+    for _ in range(R):
+        d = {k: v.to(dev) for k, v in host.items()}
+        d["C"] = torch.empty((p.M, p.N), dtype=cdt, device=dev)
+        copies.append(d)
+    log(f"{R} operand copies resident ({R * step_bytes / 2**20:.0f} MiB)")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    code = dg.out_code(p.out_dtype)
+
+    def step(i):
+        d = copies[i % R]
+        if p.grouped:
+            st = dg.dg_grouped_gemm_fp8(d["A"].data_ptr(), d["sA"].data_ptr(), d["B"].data_ptr(),
+                                        d["sB"].data_ptr(), d["C"].data_ptr(), d["offs"].data_ptr(),
+                                        p.G, p.M, p.N, p.K, code, sh)
+        else:
+            st = dg.dg_gemm_fp8_blockscaled(d["A"].data_ptr(), d["sA"].data_ptr(), d["B"].data_ptr(),
+                                            d["sB"].data_ptr(), d["C"].data_ptr(), p.M, p.N, p.K,
+                                            code, sh)
+        if st != dg.DG_OK:
+            raise dg.DGError(st, "bench step")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        ev[i].record(stream)
+        step(args.warmup + i)
+    ev[K].record(stream)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+
+    ms_step = (t_end - t_start) * 1e3 / K
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(K)])
+    kern_ms = float(ev[0].elapsed_time(ev[K])) / K
+    log(f"kernel ms (HIP events): mean {kern_ms:.4f}  p10 {np.percentile(per, 10):.4f}  "
+        f"p50 {np.percentile(per, 50):.4f}  p90 {np.percentile(per, 90):.4f}; wall ms/step {ms_step:.4f}")
+
+    flop = p.algorithmic_flop()
+    if args.workload in HBM_BOUND and args.workload == 3:
+        value = step_bytes / (ms_step * 1e-3) / 1e9
+        unit = "GB/s"
+    else:
+        value = flop / (ms_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+    if args.workload in HBM_BOUND:
+        achieved = step_bytes / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = flop / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4)}
+    roof["traffic"] = measured_traffic(p.name)
+    log(f"algorithmic: {flop / 1e9:.2f} GFLOP, {step_bytes / 2**20:.1f} MiB per step; "
+        f"TFLOP/s (kernel) {flop / (kern_ms * 1e-3) / 1e12:.1f}, "
+        f"GB/s (kernel) {step_bytes / (kern_ms * 1e-3) / 1e9:.0f}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(p)
+        if unit == "GB/s":
+            # same sample, expressed in the metric's unit (bytes of the full step
+            # scaled by the share of rows the oracle covered per second)
+            cpu = dict(cpu, value=round(cpu["value"] * 1e12 / flop * step_bytes / 1e9, 6), unit="GB/s")
+        log(f"cpu oracle: {cpu}")
+
+    cfg = {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "out_dtype": p.out_dtype,
+           "scale_block": "128x128", "seed": p.seed, "operand_copies": R}
+    if p.grouped:
+        cfg.update({"groups": p.G, "real_rows": p.real_rows})
+    line = {"metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": K,
+            "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+            "config": cfg, "roofline": roof, "cpu_baseline": cpu,
+            "kernel_ms": round(kern_ms, 5)}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

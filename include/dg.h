@@ -1,0 +1,120 @@
+/*
+ * dg.h -- C ABI of libdg.so: FP8 (E4M3) GEMM with 128x128 block scales on
+ * AMD Instinct MI355X (gfx950), dense and MoE-grouped.
+ *
+ * The operation (DeepGEMM FP8-for-MoE page, 2kiu.com/news/5461879,
+ * section 2.1 "block-wise scaling"; FP32 accumulation, section 3.3):
+ *
+ *   C[i][j] = sum over K-blocks kb of
+ *             fp32(sA[i/128][kb] * sB[j/128][kb]) * P_kb[i][j],
+ *   P_kb[i][j] = sum_{k = 128 kb}^{128 kb + 127} dec(A[i][k]) * dec(B[j][k])
+ *
+ * i.e. every 128-wide K-block's partial product is formed by the FP8 matrix
+ * cores with FP32 accumulation and then rescaled in FP32 by that block's A and
+ * B scale factors before it is added to the FP32 accumulator.  dec() is the
+ * OCP E4M3FN decode: 1 sign, 4 exponent (bias 7), 3 mantissa bits, largest
+ * finite value 448 (DeepGEMM FP8 kernel write-up, demingchina.com/news/60142,
+ * section 3.1 table).  The result is written once, as FP32 or as BF16
+ * (round to nearest even).
+ *
+ * Layout (the caller supplies A, B and both scale sets; A row-major, B
+ * column-major -- FP8-for-MoE page, section 4.3):
+ *   A  : E4M3 bytes, [M][K] row-major (K contiguous)
+ *   B  : E4M3 bytes, [N][K] row-major, i.e. the K x N operand stored
+ *        column-major (K contiguous)
+ *   sA : float32 [ceil(M/128)][K/128] row-major
+ *   sB : float32 [ceil(N/128)][K/128] row-major
+ *   C  : [M][N] row-major, float32 or bfloat16 (out_dtype)
+ *
+ * Conventions shared by every entry point:
+ *   - All data pointers are device memory owned by the caller.  The library
+ *     allocates nothing and keeps no per-call state: calls are thread-safe and
+ *     may run concurrently on different streams.
+ *   - Calls are asynchronous: the work is enqueued on `stream` (0 = the null
+ *     stream) and the call returns without synchronising.  Passing the stream
+ *     explicitly lets a caller order the GEMM against collectives on the same
+ *     stream (a race of that kind is discussed on the vLLM integration page,
+ *     mpbf.cn/news/61361, section 5.5).
+ *   - Argument errors are detected on the host before any HIP call and return
+ *     DG_ERR_INVALID_ARG: a null pointer for a non-empty operand, negative or
+ *     too large sizes (each of M, N, K must be below 2^31), an unknown
+ *     out_dtype, A / B / C not 16-byte aligned, sA / sB / group_offsets not
+ *     4-byte aligned.
+ *   - Shapes outside the supported set return DG_ERR_UNSUPPORTED: K must be a
+ *     multiple of 128 and N a multiple of 8.  M is arbitrary.
+ *   - Empty work (M == 0 or N == 0) is a no-op that returns DG_OK.  K == 0
+ *     writes zeros.
+ *   - A failed kernel launch returns DG_ERR_LAUNCH.  Faults inside a kernel
+ *     surface at the caller's next synchronisation, as for any HIP kernel.
+ *   - Out of scope: alpha / beta (C is overwritten, alpha = 1, beta = 0),
+ *     transposed layouts other than the above, other element types.
+ */
+#ifndef DG_H_
+#define DG_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DG_OUT_F32 = 0,   /* C is float32 */
+  DG_OUT_BF16 = 1   /* C is bfloat16, rounded to nearest even from FP32 */
+} dg_out_dtype;
+
+typedef enum {
+  DG_OK = 0,
+  DG_ERR_INVALID_ARG = -1,
+  DG_ERR_UNSUPPORTED = -2,
+  DG_ERR_LAUNCH = -3
+} dg_status;
+
+/*
+ * Dense block-scaled FP8 GEMM, C = A x B with 128x128 block scales
+ * (FP8-for-MoE page, section 2.1).  Shapes and layouts as above.
+ */
+int dg_gemm_fp8_blockscaled(const void* A, const float* sA,
+                            const void* B, const float* sB,
+                            void* C, int64_t M, int64_t N, int64_t K,
+                            int out_dtype, hipStream_t stream);
+
+/*
+ * MoE grouped block-scaled FP8 GEMM in one launch over contiguous per-expert
+ * row segments (the one-matrix expert layout of the shape-specialised-kernels
+ * page, nxmr.cn/news/132300, section 2.2; MoE experts share N and K while
+ * the row count varies, FP8-for-MoE page, section 2.2).
+ *
+ *   A             : E4M3 [M_total][K]; rows [o_e, o_{e+1}) belong to expert e
+ *   sA            : float32 [M_total/128][K/128]
+ *   B             : E4M3 [num_groups][N][K] (expert e's B_e, K contiguous)
+ *   sB            : float32 [num_groups][ceil(N/128)][K/128]
+ *   C             : [M_total][N] float32 or bfloat16
+ *   group_offsets : DEVICE int32 [num_groups + 1] with
+ *                   0 = o_0 <= o_1 <= ... <= o_G = M_total, every o_e a
+ *                   multiple of 128 (segments are padded to 128 rows, so a
+ *                   128-row tile or an A scale block never mixes experts).
+ *                   Empty experts (o_e == o_{e+1}) are allowed.
+ *
+ * Rows of a segment that the caller padded with zero codes come out as
+ * exact zeros.  The offsets live on the device and are not validated (that
+ * would need a device-to-host synchronisation): offsets that break the rules
+ * above give undefined results.  Host-side errors: num_groups < 1 or
+ * M_total not a multiple of 128 -> DG_ERR_INVALID_ARG; the shared rules
+ * above otherwise.
+ */
+int dg_grouped_gemm_fp8(const void* A, const float* sA,
+                        const void* B, const float* sB,
+                        void* C, const int32_t* group_offsets,
+                        int num_groups, int64_t M_total, int64_t N, int64_t K,
+                        int out_dtype, hipStream_t stream);
+
+/* Static, NUL-terminated description of a dg_status value. */
+const char* dg_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H_ */

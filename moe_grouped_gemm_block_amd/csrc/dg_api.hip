@@ -1,0 +1,118 @@
+// Host side of libdg.so: argument checks, kernel choice and launch.
+//
+// Every check that can be made without touching the device happens here,
+// before any HIP call, so that argument errors are reported synchronously
+// and the same checks run on a machine without a GPU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dg.h"
+#include "gemm_f16mma.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shared checks of both entry points.  rows = M (dense) or M_total (grouped).
+int check_common(const void* A, const float* sA, const void* B, const float* sB, void* C,
+                 int64_t rows, int64_t N, int64_t K, int out_dtype) {
+  if (rows < 0 || N < 0 || K < 0 || rows > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return DG_ERR_INVALID_ARG;
+  if (out_dtype != DG_OUT_F32 && out_dtype != DG_OUT_BF16) return DG_ERR_INVALID_ARG;
+  if (rows == 0 || N == 0) return DG_OK;
+  if (C == nullptr || !aligned(C, 16)) return DG_ERR_INVALID_ARG;
+  if (K > 0) {
+    if (A == nullptr || B == nullptr || sA == nullptr || sB == nullptr) return DG_ERR_INVALID_ARG;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(sA, 4) || !aligned(sB, 4))
+      return DG_ERR_INVALID_ARG;
+  }
+  if (K % dg::KBLK != 0 || N % 8 != 0) return DG_ERR_UNSUPPORTED;
+  return DG_OK;
+}
+
+// Tile shape of one launch.  128 x 256 tiles give each wave a 64 x 128
+// sub-tile (the best operand reuse the register file allows); narrower
+// problems, or ones that would leave most CUs idle, take 128 x 128 tiles.
+constexpr int kCUs = 256;
+
+template <int BM, int BN>
+int launch_tiles(dg::GemmArgs a, void (*k_bf16)(dg::GemmArgs), void (*k_f32)(dg::GemmArgs),
+                 int out_dtype, hipStream_t stream) {
+  a.m_tiles = int((int64_t(a.M) + BM - 1) / BM);
+  a.n_tiles = int((int64_t(a.N) + BN - 1) / BN);
+  const int64_t blocks = int64_t(a.m_tiles) * a.n_tiles;
+  if (blocks <= 0) return DG_OK;
+  if (blocks > INT32_MAX) return DG_ERR_UNSUPPORTED;
+  void* kargs[] = {&a};
+  const void* fn = out_dtype == DG_OUT_BF16 ? reinterpret_cast<const void*>(k_bf16)
+                                            : reinterpret_cast<const void*>(k_f32);
+  hipError_t err = hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(256), kargs, 0, stream);
+  return err == hipSuccess ? DG_OK : DG_ERR_LAUNCH;
+}
+
+int launch(const dg::GemmArgs& a, int out_dtype, hipStream_t stream) {
+  const int64_t m_tiles = (int64_t(a.M) + 127) / 128;
+  const int64_t wide = m_tiles * ((int64_t(a.N) + 255) / 256);
+  if (a.N > 128 && wide >= kCUs)
+    return launch_tiles<128, 256>(a, dg::dg_gemm_128x256_bf16, dg::dg_gemm_128x256_f32, out_dtype, stream);
+  return launch_tiles<128, 128>(a, dg::dg_gemm_128x128_bf16, dg::dg_gemm_128x128_f32, out_dtype, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dg_gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const float* sB,
+                            void* C, int64_t M, int64_t N, int64_t K, int out_dtype,
+                            hipStream_t stream) {
+  int st = check_common(A, sA, B, sB, C, M, N, K, out_dtype);
+  if (st != DG_OK || M == 0 || N == 0) return st;
+  dg::GemmArgs a{};
+  a.A = static_cast<const uint8_t*>(A);
+  a.sA = sA;
+  a.B = static_cast<const uint8_t*>(B);
+  a.sB = sB;
+  a.C = C;
+  a.offs = nullptr;
+  a.G = 1;
+  a.M = int(M);
+  a.N = int(N);
+  a.K = int(K);
+  return launch(a, out_dtype, stream);
+}
+
+int dg_grouped_gemm_fp8(const void* A, const float* sA, const void* B, const float* sB, void* C,
+                        const int32_t* group_offsets, int num_groups, int64_t M_total,
+                        int64_t N, int64_t K, int out_dtype, hipStream_t stream) {
+  if (num_groups < 1) return DG_ERR_INVALID_ARG;
+  if (M_total < 0 || M_total % dg::KBLK != 0) return DG_ERR_INVALID_ARG;
+  int st = check_common(A, sA, B, sB, C, M_total, N, K, out_dtype);
+  if (st != DG_OK || M_total == 0 || N == 0) return st;
+  if (group_offsets == nullptr || !aligned(group_offsets, 4)) return DG_ERR_INVALID_ARG;
+  dg::GemmArgs a{};
+  a.A = static_cast<const uint8_t*>(A);
+  a.sA = sA;
+  a.B = static_cast<const uint8_t*>(B);
+  a.sB = sB;
+  a.C = C;
+  a.offs = group_offsets;
+  a.G = num_groups;
+  a.M = int(M_total);
+  a.N = int(N);
+  a.K = int(K);
+  return launch(a, out_dtype, stream);
+}
+
+const char* dg_status_string(int status) {
+  switch (status) {
+    case DG_OK: return "DG_OK: success";
+    case DG_ERR_INVALID_ARG: return "DG_ERR_INVALID_ARG: invalid argument (null, misaligned, negative or oversized)";
+    case DG_ERR_UNSUPPORTED: return "DG_ERR_UNSUPPORTED: shape not supported (K % 128 != 0 or N % 8 != 0)";
+    case DG_ERR_LAUNCH: return "DG_ERR_LAUNCH: kernel launch failed";
+    default: return "unknown dg_status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,284 @@
+// FP8 block-scaled GEMM kernel for gfx950 (dense and MoE-grouped).
+//
+// What it computes: for every 128-wide K-block, the exact products of the
+// E4M3 operands summed with FP32-grade accumulation, rescaled in FP32 by
+// fp32(sA * sB) of that block and added to an FP32 accumulator (block-wise
+// scaling of the DeepGEMM FP8-for-MoE page, 2kiu.com/news/5461879, sections
+// 2.1 and 3.3).
+//
+// Why FP16 matrix cores.  On gfx950 the FP8 MFMA sums the products of every
+// group of 8 consecutive K elements inside a window of about 14 bits below
+// the largest product of the group and drops whatever lies below it; on
+// Gaussian blocks that alone reaches ~1.7e-5 of sum|a b|, and far more on
+// blocks with a wide spread of magnitudes.  The FP16 MFMA keeps a 24-bit
+// window, i.e. it accumulates like FP32.  Every E4M3 value is exactly an
+// FP16 value, so converting the fragments (v_cvt_scalef32_pk_f16_fp8, two
+// values per instruction, scale 1) loses nothing and the FP16 matrix cores
+// then deliver the block partials that the definition asks for.  (The pages'
+// Hopper kernels promote FP8 tensor-core partials to FP32 registers every
+// K-block for the same kind of reason: FP8 MMA accumulation is narrow.)
+//
+// Structure (tiling of the DeepGEMM FP8 kernel write-up, demingchina.com/
+// news/60142, sections 2.3 and 3.3-4.3, re-planned for CDNA4):
+//   * one workgroup = 4 waves = a BM x BN tile of C, waves 2 x 2, each wave a
+//     (BM/2) x (BN/2) sub-tile;
+//   * A and B stay FP8 in HBM and LDS.  Each K-block's tiles are copied
+//     straight into LDS with 16-byte global->LDS loads (no VGPR staging), two
+//     stages (double buffering: the next block streams in while the current
+//     one is multiplied);
+//   * inside a 128-byte LDS row, 16-byte granules are XOR-swizzled (see
+//     common.hpp) so fragment reads do not collide on banks;
+//   * B rows are permuted on their way into LDS so that, with B as the MFMA's
+//     first operand, every lane ends up holding (BN/8) consecutive columns of
+//     one output row: the epilogue writes whole 16-byte vectors;
+//   * per K-block and wave: FP8 fragments -> FP16 in registers, 4 chained
+//     16x16x32 FP16 MFMAs per 16x16 output tile give the block partial P,
+//     then acc = fma(sA*sB, P, acc) in FP32.  With 128-row scale blocks and
+//     wave sub-tiles that never straddle them, sA*sB is one scalar per wave;
+//   * tiles are ordered so that each XCD (own L2) works on a compact group of
+//     row and column tiles.
+#pragma once
+
+#include "common.hpp"
+
+namespace dg {
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+// Four E4M3 bytes -> four FP16 values (exact), as two packed pairs.
+__device__ __forceinline__ void fp8x4_to_f16(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(w), 1.0f, false);
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(w), 1.0f, true);
+  lo = __builtin_bit_cast(uint32_t, a);
+  hi = __builtin_bit_cast(uint32_t, b);
+}
+
+// 32 FP8 bytes of one fragment row -> the four FP16 MFMA operands of the
+// K-block (operand s holds bytes 8s .. 8s+7).
+__device__ __forceinline__ void fp8x32_to_f16(const int4& r0, const int4& r1, v8h out[4]) {
+  const uint32_t w[8] = {uint32_t(r0.x), uint32_t(r0.y), uint32_t(r0.z), uint32_t(r0.w),
+                         uint32_t(r1.x), uint32_t(r1.y), uint32_t(r1.z), uint32_t(r1.w)};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    uint32_t h[4];
+    fp8x4_to_f16(w[2 * s], h[0], h[1]);
+    fp8x4_to_f16(w[2 * s + 1], h[2], h[3]);
+    out[s] = __builtin_bit_cast(v8h, (uint4{h[0], h[1], h[2], h[3]}));
+  }
+}
+
+__device__ __forceinline__ v4f mfma16_f16(const v8h& a, const v8h& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(0) (expcnt / lgkmcnt left at their maxima): waits for this
+// wave's outstanding global->LDS copies.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+struct GemmArgs {
+  const uint8_t* A;       // [M][K]
+  const float* sA;        // [ceil(M/128)][K/128]
+  const uint8_t* B;       // [G][N][K]
+  const float* sB;        // [G][ceil(N/128)][K/128]
+  void* C;                // [M][N]
+  const int32_t* offs;    // [G+1] device, or nullptr for dense
+  int G;
+  int M, N, K;
+  int m_tiles, n_tiles;
+};
+
+// Tile order: blockIdx -> (m-tile, n-tile).  Workgroups are dealt to the 8
+// XCDs round-robin; consecutive "local" indices on one XCD walk a group of
+// GROUP_M row tiles column by column, so the tiles that run together on an
+// XCD share A rows and B columns in its L2.
+template <int GROUP_M>
+__device__ __forceinline__ void tile_of(int bid, int m_tiles, int n_tiles, int& tm, int& tn) {
+  const int T = m_tiles * n_tiles;
+  int t = bid;
+  if ((T & 7) == 0) t = (bid & 7) * (T >> 3) + (bid >> 3);
+  const int per_group = GROUP_M * n_tiles;
+  const int g = t / per_group;
+  const int first_m = g * GROUP_M;
+  const int gsize = min(GROUP_M, m_tiles - first_m);
+  const int r = t - g * per_group;
+  tm = first_m + r % gsize;
+  tn = r / gsize;
+}
+
+template <int BM, int BN, bool OUT_BF16>
+__device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
+  constexpr int WM = BM / 2, WN = BN / 2;      // wave sub-tile
+  constexpr int MI = WM / 16, NI = WN / 16;    // 16x16 MFMA tiles per wave
+  constexpr int STAGE = (BM + BN) * KBLK;      // bytes per LDS stage
+  static_assert(BM % 32 == 0 && BN % 64 == 0 && WN <= 128 && WM <= 128, "tile shape");
+  static_assert(WN % 64 == 0 || WN == 32, "column permutation needs WN/4 a multiple of 8");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int tm, tn;
+  tile_of<8>(blockIdx.x, p.m_tiles, p.n_tiles, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int M = p.M, N = p.N, K = p.K;
+  const int Kb = K / KBLK;
+  const int Nb = (N + KBLK - 1) / KBLK;
+
+  int e = 0;
+  if (p.offs != nullptr) {
+    e = find_group(p.offs, p.G, m0);
+    if (e >= p.G) return;                      // uniform across the workgroup
+  }
+  const uint8_t* __restrict__ Ag = p.A;
+  const uint8_t* __restrict__ Bg = p.B + (size_t)e * N * K;
+
+  const int wm = (wave >> 1) * WM;             // wave sub-tile origin in the tile
+  const int wn = (wave & 1) * WN;
+  // scale rows of this wave (clamped: a wave wholly past the edge stores nothing)
+  const int mb = min((m0 + wm) / KBLK, (M - 1) / KBLK);
+  const int nb = min((n0 + wn) / KBLK, Nb - 1);
+  const float* __restrict__ sAr = p.sA + (size_t)mb * Kb;
+  const float* __restrict__ sBr = p.sB + ((size_t)e * Nb + nb) * Kb;
+
+  // ---- per-lane source rows of the global->LDS copies ----------------------
+  // Chunk c covers LDS rows 8c .. 8c+7 of a tile (1 KB); lane L fills row
+  // 8c + L/8, slot L%8, with global granule (L%8) ^ swizzle(row).
+  constexpr int A_CH = BM / 8 / 4, B_CH = BN / 8 / 4;   // chunks per wave
+  const uint8_t* a_src[A_CH];
+  const uint8_t* b_src[B_CH];
+  int a_dst[A_CH], b_dst[B_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int c = wave + 4 * i;
+    const int r = 8 * c + (lane >> 3);
+    const int g = (lane & 7) ^ ((r ^ (r >> 3)) & 7);
+    const int gm = min(m0 + r, M - 1);         // rows past M only feed rows that are never stored
+    a_src[i] = Ag + (size_t)gm * K + g * 16;
+    a_dst[i] = 8 * c * KBLK;
+  }
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int c = wave + 4 * i;
+    const int r = 8 * c + (lane >> 3);         // LDS row in the B tile
+    const int half = r / WN, pr = r % WN;      // wave column half, row inside it
+    const int ii = pr % 16, ni = pr / 16;      // MFMA operand row ii of column tile ni
+    const int nl = (ii >> 2) * (WN / 4) + ni * 4 + (ii & 3);
+    const int g = (lane & 7) ^ ((r ^ (r >> 3)) & 7);
+    const int gn = min(n0 + half * WN + nl, N - 1);
+    b_src[i] = Bg + (size_t)gn * K + g * 16;
+    b_dst[i] = BM * KBLK + 8 * c * KBLK;
+  }
+
+  auto issue_copies = [&](int kb, int stage) {
+    uint8_t* base = lds + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i)
+      __builtin_amdgcn_global_load_lds(a_src[i] + (size_t)kb * KBLK,
+                                       (__attribute__((address_space(3))) void*)(base + a_dst[i]),
+                                       16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i)
+      __builtin_amdgcn_global_load_lds(b_src[i] + (size_t)kb * KBLK,
+                                       (__attribute__((address_space(3))) void*)(base + b_dst[i]),
+                                       16, 0, 0);
+  };
+
+  v4f acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int q = lane >> 4;                     // 32-byte K chunk of this lane
+  const int r16 = lane & 15;
+
+  if (Kb > 0) {
+    issue_copies(0, 0);
+    wait_vmem();
+    __syncthreads();
+  }
+
+  for (int kb = 0; kb < Kb; ++kb) {
+    const int stage = kb & 1;
+    if (kb + 1 < Kb) issue_copies(kb + 1, stage ^ 1);
+    const float s = sAr[kb] * sBr[kb];
+    const uint8_t* la = lds + stage * STAGE;
+    const uint8_t* lb = la + BM * KBLK;
+
+    // A fragments (MFMA second operand): rows wm + 16 mi + r16, bytes [32q, 32q+32)
+    v8h af[MI][4];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int r = wm + mi * 16 + r16;
+      const int4 x0 = *reinterpret_cast<const int4*>(la + r * KBLK + swz(r, 2 * q) * 16);
+      const int4 x1 = *reinterpret_cast<const int4*>(la + r * KBLK + swz(r, 2 * q + 1) * 16);
+      fp8x32_to_f16(x0, x1, af[mi]);
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int r = wn + ni * 16 + r16;
+      const int4 y0 = *reinterpret_cast<const int4*>(lb + r * KBLK + swz(r, 2 * q) * 16);
+      const int4 y1 = *reinterpret_cast<const int4*>(lb + r * KBLK + swz(r, 2 * q + 1) * 16);
+      v8h bf[4];
+      fp8x32_to_f16(y0, y1, bf);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        v4f part = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) part = mfma16_f16(bf[st], af[mi][st], part);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[mi][ni][r] = __builtin_fmaf(s, part[r], acc[mi][ni][r]);
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds C[m][n0 + wn + q*(WN/4) + 0 .. WN/4-1] --------
+  constexpr int CW = WN / 4;                   // consecutive columns per lane
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int m = m0 + wm + mi * 16 + r16;
+    if (m >= M) continue;
+    const int nbase = n0 + wn + q * CW;
+    float v[CW];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[ni * 4 + r] = acc[mi][ni][r];
+    if constexpr (OUT_BF16) {
+      uint16_t* row = reinterpret_cast<uint16_t*>(p.C) + (size_t)m * N;
+#pragma unroll
+      for (int c = 0; c < CW / 8; ++c) {
+        const int n = nbase + 8 * c;
+        if (n >= N) continue;                  // N % 8 == 0: whole vector in range
+        uint4 w;
+        w.x = pack_bf16x2(v[8 * c + 0], v[8 * c + 1]);
+        w.y = pack_bf16x2(v[8 * c + 2], v[8 * c + 3]);
+        w.z = pack_bf16x2(v[8 * c + 4], v[8 * c + 5]);
+        w.w = pack_bf16x2(v[8 * c + 6], v[8 * c + 7]);
+        *reinterpret_cast<uint4*>(row + n) = w;
+      }
+    } else {
+      float* row = reinterpret_cast<float*>(p.C) + (size_t)m * N;
+#pragma unroll
+      for (int c = 0; c < CW / 4; ++c) {
+        const int n = nbase + 4 * c;
+        if (n >= N) continue;
+        *reinterpret_cast<float4*>(row + n) = float4{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
+      }
+    }
+  }
+}
+
+// Named kernels (one per tile shape and output type) around the body.
+#define DG_GEMM_KERNEL(NAME, BM, BN, BF16) \
+  __global__ __launch_bounds__(256, 1) void NAME(GemmArgs p) { gemm_f16mma_body<BM, BN, BF16>(p); }
+DG_GEMM_KERNEL(dg_gemm_128x256_bf16, 128, 256, true)
+DG_GEMM_KERNEL(dg_gemm_128x256_f32, 128, 256, false)
+DG_GEMM_KERNEL(dg_gemm_128x128_bf16, 128, 128, true)
+DG_GEMM_KERNEL(dg_gemm_128x128_f32, 128, 128, false)
+#undef DG_GEMM_KERNEL
+
+}  // namespace dg

@@ -1,0 +1,161 @@
+"""ctypes binding of libdg.so (argument marshalling only).
+
+The functions named like the C entry points take raw integers (device
+addresses, sizes, a hipStream_t handle) and return the dg_status code.  The
+torch-facing helpers below them only check dtypes / shapes / devices, pass
+``data_ptr()`` values and the current stream, and raise on a non-zero status;
+every step of the computation runs in the library's HIP kernels.
+
+Loading fails loudly when the library has not been built: there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("DG_LIBRARY", os.path.join(_PKG, "libdg.so"))
+
+DG_OUT_F32 = 0
+DG_OUT_BF16 = 1
+DG_OK = 0
+DG_ERR_INVALID_ARG = -1
+DG_ERR_UNSUPPORTED = -2
+DG_ERR_LAUNCH = -3
+
+EXPORTED = ("dg_gemm_fp8_blockscaled", "dg_grouped_gemm_fp8", "dg_status_string")
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdg.so once; raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m moe_grouped_gemm_block_amd.build` "
+                "(there is no non-HIP fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.dg_gemm_fp8_blockscaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, vp]
+        L.dg_gemm_fp8_blockscaled.restype = ci
+        L.dg_grouped_gemm_fp8.argtypes = [vp, vp, vp, vp, vp, vp, ci, i64, i64, i64, ci, vp]
+        L.dg_grouped_gemm_fp8.restype = ci
+        L.dg_status_string.argtypes = [ci]
+        L.dg_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------- raw C names
+
+def dg_gemm_fp8_blockscaled(A, sA, B, sB, C, M, N, K, out_dtype, stream) -> int:
+    return lib().dg_gemm_fp8_blockscaled(A, sA, B, sB, C, M, N, K, out_dtype, stream)
+
+
+def dg_grouped_gemm_fp8(A, sA, B, sB, C, group_offsets, num_groups, M_total, N, K,
+                        out_dtype, stream) -> int:
+    return lib().dg_grouped_gemm_fp8(A, sA, B, sB, C, group_offsets, num_groups, M_total,
+                                     N, K, out_dtype, stream)
+
+
+def dg_status_string(status: int) -> str:
+    return lib().dg_status_string(status).decode()
+
+
+class DGError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {dg_status_string(status)} ({status})")
+        self.status = status
+
+
+# ---------------------------------------------------------------- torch helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check_fp8(t, name):
+    torch = _torch()
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError(f"{name} must be uint8 E4M3 codes or float8_e4m3fn, got {t.dtype}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+def _check_f32(t, name, shape):
+    torch = _torch()
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _out(C, rows, N, out_dtype, like):
+    torch = _torch()
+    dt = torch.float32 if out_dtype == DG_OUT_F32 else torch.bfloat16
+    if C is None:
+        return torch.empty((rows, N), dtype=dt, device=like.device)
+    if C.dtype != dt or tuple(C.shape) != (rows, N) or not C.is_contiguous():
+        raise ValueError("C has the wrong dtype, shape or layout")
+    return C
+
+
+def out_code(out_dtype) -> int:
+    if out_dtype in (DG_OUT_F32, "f32", "float32"):
+        return DG_OUT_F32
+    if out_dtype in (DG_OUT_BF16, "bf16", "bfloat16"):
+        return DG_OUT_BF16
+    raise ValueError(f"unknown out_dtype {out_dtype!r}")
+
+
+def _stream(stream):
+    if stream is None:
+        return _torch().cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def gemm_fp8_blockscaled(A, sA, B, sB, out_dtype="bf16", C=None, stream=None):
+    """C[M][N] = block-scaled A[M][K] x B (stored [N][K]) on the device."""
+    _check_fp8(A, "A")
+    _check_fp8(B, "B")
+    M, K = A.shape
+    N, K2 = B.shape
+    if K != K2:
+        raise ValueError("A and B must share K")
+    _check_f32(sA, "sA", (-(-M // 128), K // 128))
+    _check_f32(sB, "sB", (-(-N // 128), K // 128))
+    code = out_code(out_dtype)
+    C = _out(C, M, N, code, A)
+    st = dg_gemm_fp8_blockscaled(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(),
+                                 C.data_ptr(), M, N, K, code, _stream(stream))
+    if st != DG_OK:
+        raise DGError(st, "dg_gemm_fp8_blockscaled")
+    return C
+
+
+def grouped_gemm_fp8(A, sA, B, sB, group_offsets, out_dtype="bf16", C=None, stream=None):
+    """MoE grouped GEMM over contiguous 128-row-padded expert segments."""
+    torch = _torch()
+    _check_fp8(A, "A")
+    _check_fp8(B, "B")
+    M_total, K = A.shape
+    G, N, K2 = B.shape
+    if K != K2:
+        raise ValueError("A and B must share K")
+    _check_f32(sA, "sA", (M_total // 128, K // 128))
+    _check_f32(sB, "sB", (G, -(-N // 128), K // 128))
+    if (group_offsets.dtype != torch.int32 or not group_offsets.is_cuda
+            or tuple(group_offsets.shape) != (G + 1,)):
+        raise ValueError("group_offsets must be a device int32 tensor of G + 1 entries")
+    code = out_code(out_dtype)
+    C = _out(C, M_total, N, code, A)
+    st = dg_grouped_gemm_fp8(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(),
+                             C.data_ptr(), group_offsets.data_ptr(), G, M_total, N, K, code,
+                             _stream(stream))
+    if st != DG_OK:
+        raise DGError(st, "dg_grouped_gemm_fp8")
+    return C

@@ -1,0 +1,110 @@
+"""C-ABI of libdg.so on the host: exports and argument validation (CPU only).
+
+Every call below fails validation (or is empty work) and returns before any
+HIP call, so no GPU is needed.  The fake device addresses are never
+dereferenced.
+"""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+from moe_grouped_gemm_block_amd import dg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, INVALID, UNSUP = dg.DG_OK, dg.DG_ERR_INVALID_ARG, dg.DG_ERR_UNSUPPORTED
+P = 1 << 20          # a 16-byte aligned fake address, never dereferenced
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        names |= set(re.findall(r"\b(dg_\w+)\s*\(", src))
+    return names
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(dg.LIB_PATH):
+        from moe_grouped_gemm_block_amd import build
+        build.build(verbose=False)
+    return dg.lib()
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() >= {"dg_gemm_fp8_blockscaled", "dg_grouped_gemm_fp8",
+                                    "dg_status_string"}
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", dg.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\sT\s+(dg_\w+)", out))
+    assert declared_functions() <= exported
+    assert set(dg.EXPORTED) == declared_functions()
+
+
+def test_status_strings(L):
+    for st in (OK, INVALID, UNSUP, dg.DG_ERR_LAUNCH):
+        assert dg.dg_status_string(st).startswith("DG_")
+    assert "unknown" in dg.dg_status_string(42)
+
+
+def dense(A=P, sA=P, B=P, sB=P, C=P, M=256, N=256, K=256, out=1):
+    return dg.dg_gemm_fp8_blockscaled(A, sA, B, sB, C, M, N, K, out, None)
+
+
+def grouped(A=P, sA=P, B=P, sB=P, C=P, offs=P, G=4, M=512, N=256, K=256, out=1):
+    return dg.dg_grouped_gemm_fp8(A, sA, B, sB, C, offs, G, M, N, K, out, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(A=None), INVALID), (dict(B=None), INVALID), (dict(sA=None), INVALID),
+    (dict(sB=None), INVALID), (dict(C=None), INVALID),
+    (dict(M=-1), INVALID), (dict(N=-8), INVALID), (dict(K=-128), INVALID),
+    (dict(M=1 << 31), INVALID), (dict(K=1 << 40), INVALID),
+    (dict(out=2), INVALID), (dict(out=-1), INVALID),
+    (dict(A=P + 8), INVALID), (dict(B=P + 4), INVALID), (dict(C=P + 2), INVALID),
+    (dict(sA=P + 2), INVALID), (dict(sB=P + 1), INVALID),
+    (dict(K=200), UNSUP), (dict(K=64), UNSUP), (dict(N=100), UNSUP), (dict(N=12), UNSUP),
+    (dict(M=0), OK), (dict(N=0), OK), (dict(M=0, A=None, C=None), OK),
+])
+def test_dense_validation(L, kw, want):
+    assert dense(**kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(G=0), INVALID), (dict(G=-3), INVALID), (dict(M=300), INVALID), (dict(M=-128), INVALID),
+    (dict(offs=None), INVALID), (dict(offs=P + 2), INVALID), (dict(A=None), INVALID),
+    (dict(out=7), INVALID), (dict(K=100), UNSUP), (dict(N=20), UNSUP),
+    (dict(M=0), OK), (dict(N=0), OK),
+])
+def test_grouped_validation(L, kw, want):
+    assert grouped(**kw) == want
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The package never imports the oracle, and the oracle never imports the package."""
+    pkg = os.path.join(ROOT, "moe_grouped_gemm_block_amd")
+    for f in glob.glob(os.path.join(pkg, "**", "*.py"), recursive=True):
+        assert not re.search(r"^\s*(from|import)\s+oracle", open(f).read(), re.M), f
+    for f in glob.glob(os.path.join(pkg, "csrc", "*")):
+        assert "oracle" not in open(f).read(), f
+    for f in glob.glob(os.path.join(ROOT, "oracle", "*.py")):
+        assert "moe_grouped_gemm_block_amd" not in open(f).read(), f
+
+
+def test_binding_refuses_missing_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(dg, "_lib", None)
+    monkeypatch.setattr(dg, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        dg.lib()

@@ -1,0 +1,220 @@
+"""Parity of the HIP path (through the C-ABI) with the CPU oracle.  Needs a GPU.
+
+Bar (per element): |C_gpu - C_ref| <= 1e-5 * mass + 1e-6 for FP32 output,
+plus 2^-8 * |C_ref| for BF16 output, where mass = sum |a b sA sB|.  Small
+shapes are compared in full; the full-size workloads on sampled rows (all
+columns), always including first / last rows of tiles and segments.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_grouped_gemm_block_amd import dg
+from moe_grouped_gemm_block_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    dg.lib()                      # fail loudly if the HIP library is missing
+
+
+def to_dev(p: I.Problem):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    d = dict(A=t(p.A), sA=t(p.sA), B=t(p.B), sB=t(p.sB))
+    if p.grouped:
+        d["offs"] = t(p.group_offsets.astype(np.int32))
+    return d
+
+
+def run(p: I.Problem, d=None, C=None):
+    d = d or to_dev(p)
+    if p.grouped:
+        C = dg.grouped_gemm_fp8(d["A"], d["sA"], d["B"], d["sB"], d["offs"], p.out_dtype, C=C)
+    else:
+        C = dg.gemm_fp8_blockscaled(d["A"], d["sA"], d["B"], d["sB"], p.out_dtype, C=C)
+    torch.cuda.synchronize()
+    return C
+
+
+def as64(C):
+    return C.float().cpu().numpy().astype(np.float64)
+
+
+def check(p: I.Problem, Cg: np.ndarray, rows=None, cols=None, what=""):
+    if p.grouped:
+        Cr, mass = oracle.grouped_gemm(p.A, p.sA, p.B, p.sB, p.group_offsets, rows=rows, cols=cols)
+    else:
+        Cr, mass = oracle.gemm_blockscaled(p.A, p.sA, p.B, p.sB, rows=rows, cols=cols)
+    if rows is not None:
+        Cg = Cg[rows]
+    if cols is not None:
+        Cg = Cg[:, cols]
+    bound = oracle.tolerance(Cr, mass, p.out_dtype)
+    err = np.abs(Cg - Cr)
+    ratio = float((err / bound).max()) if err.size else 0.0
+    log(f"  {what or p.name}: max err/bound = {ratio:.3g}")
+    assert np.all(np.isfinite(Cg))
+    bad = np.argwhere(err > bound)
+    assert len(bad) == 0, f"{len(bad)} elements out of tolerance, first {bad[:5].tolist()}"
+    return ratio
+
+
+def sample_rows(M, extra=(), n=64, seed=0):
+    rng = np.random.default_rng(seed)
+    edges = [r for t in range(0, M, 128) for r in (t, t + 127) if r < M]
+    pick = set(rng.choice(M, size=min(n, M), replace=False).tolist())
+    pick |= set(edges[:: max(1, len(edges) // 32)])
+    pick |= {0, M - 1, *[r for r in extra if 0 <= r < M]}
+    return np.array(sorted(pick))
+
+
+# ----------------------------------------------------------------- small shapes
+
+SMALL = [(1, 8, 128), (63, 136, 128), (64, 256, 256), (65, 264, 384), (127, 128, 128),
+         (128, 392, 256), (129, 96, 512), (300, 520, 384), (256, 256, 256)]
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_dense_small_full(M, N, K, out):
+    log(f"dense small M={M} N={N} K={K} out={out}")
+    p = I.dense_problem(M, N, K, seed=M * 7 + N + K, out_dtype=out, block_log2_range=3.0)
+    check(p, as64(run(p)), what=f"{M}x{N}x{K} {out}")
+
+
+def test_config1_full():
+    p = I.make_config(1)
+    log("workload 1 (256^3, f32)")
+    check(p, as64(run(p)))
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_grouped_small_full(out):
+    log(f"grouped small out={out}")
+    p = I.grouped_problem(G=6, N=264, K=384, T=500, seed=11, popularity="zipf",
+                          zero_lowest=2, out_dtype=out)
+    assert (np.diff(p.group_offsets) == 0).any()
+    Cg = as64(run(p))
+    check(p, Cg)
+
+
+def test_grouped_single_group_matches_dense():
+    log("grouped G=1 vs dense")
+    p = I.dense_problem(384, 256, 256, seed=3, out_dtype="f32")
+    d = to_dev(p)
+    Cd = run(p, d)
+    offs = torch.tensor([0, 384], dtype=torch.int32, device=DEV)
+    Cgr = dg.grouped_gemm_fp8(d["A"], d["sA"], d["B"].unsqueeze(0).contiguous(),
+                              d["sB"].unsqueeze(0).contiguous(), offs, "f32")
+    torch.cuda.synchronize()
+    assert torch.equal(Cd, Cgr)
+
+
+def test_integer_operands_exact_in_fp32():
+    """Integer E4M3 values with power-of-two scales: every partial and every
+    rescaled sum is exactly representable, so FP32 output must be exact."""
+    log("integer exactness")
+    rng = np.random.default_rng(21)
+    M, N, K = 256, 384, 512
+    vals = np.arange(-8, 9).astype(np.float32)
+    Af = rng.choice(vals, size=(M, K)).astype(np.float32)
+    Bf = rng.choice(vals, size=(N, K)).astype(np.float32)
+    code = lambda x: torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    sA = np.exp2(rng.integers(-3, 4, size=(2, 4))).astype(np.float32)
+    sB = np.exp2(rng.integers(-3, 4, size=(3, 4))).astype(np.float32)
+    p = I.Problem("int", code(Af), sA, code(Bf), sB, M, N, K, "f32", 0)
+    Cg = as64(run(p))
+    Cr, _ = oracle.gemm_blockscaled(p.A, p.sA, p.B, p.sB)
+    assert np.abs(Cr).max() < 2 ** 24
+    np.testing.assert_array_equal(Cg, Cr)
+
+
+def test_k_zero_writes_zeros_and_empty_is_noop():
+    log("K = 0 / M = 0")
+    A = torch.empty((64, 0), dtype=torch.uint8, device=DEV)
+    B = torch.empty((128, 0), dtype=torch.uint8, device=DEV)
+    sA = torch.empty((1, 0), dtype=torch.float32, device=DEV)
+    sB = torch.empty((1, 0), dtype=torch.float32, device=DEV)
+    C = torch.full((64, 128), 7.0, device=DEV)
+    dg.gemm_fp8_blockscaled(A, sA, B, sB, "f32", C=C)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(C) == 0
+    st = dg.dg_gemm_fp8_blockscaled(0, 0, 0, 0, 0, 0, 128, 128, 0, None)
+    assert st == dg.DG_OK
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_guard_bands_untouched(out):
+    """C is placed inside a larger buffer filled with a canary; nothing
+    outside [M][N] may change (catches out-of-bounds stores)."""
+    log(f"guard bands {out}")
+    M, N, K = 129, 264, 256
+    p = I.dense_problem(M, N, K, seed=5, out_dtype=out)
+    d = to_dev(p)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    pad = 4096
+    buf = torch.full((pad + M * N + pad,), -12345.0, dtype=dt, device=DEV)
+    C = buf[pad:pad + M * N].view(M, N)
+    run(p, d, C=C)
+    assert torch.all(buf[:pad] == -12345.0) and torch.all(buf[pad + M * N:] == -12345.0)
+    check(p, as64(C), what=f"guard {out}")
+
+
+def test_repeatable_bitwise():
+    log("determinism")
+    p = I.dense_problem(512, 1024, 1024, seed=9, block_log2_range=4.0)
+    d = to_dev(p)
+    a = run(p, d).clone()
+    b = run(p, d)
+    assert torch.equal(a, b)
+
+
+# ----------------------------------------------------------------- full-size workloads
+
+@functools.lru_cache(maxsize=1)
+def workload(i):
+    return I.make_config(i)
+
+
+def test_config2_dense_4096_sampled():
+    log("workload 2 (4096^3, bf16)")
+    p = workload(2)
+    Cg = as64(run(p))
+    check(p, Cg, rows=sample_rows(p.M, n=48))
+
+
+def test_config3_skinny_full():
+    log("workload 3 (64 x 12288 x 4096, bf16)")
+    p = workload(3)
+    Cg = as64(run(p))
+    check(p, Cg)
+
+
+@pytest.mark.parametrize("i", [4, 5])
+def test_grouped_configs_sampled(i):
+    log(f"workload {i} (grouped)")
+    p = workload(i)
+    Cg = as64(run(p))
+    off = p.group_offsets
+    extra = [o for o in off[1:-1]] + [o - 1 for o in off[1:]]
+    rows = sample_rows(p.M, extra=extra, n=48, seed=i)
+    check(p, Cg, rows=rows)
+    # padding rows (zero codes) must come out exactly zero
+    _, _, counts = I.route(p.G, p.real_rows // 2, I.streams(p.seed)[3],
+                           "uniform" if i == 4 else "zipf")
+    for e in range(p.G):
+        lo = off[e] + counts[e]
+        assert np.all(Cg[lo:off[e + 1]] == 0)
