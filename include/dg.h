@@ -9,9 +9,10 @@
  *             fp32(sA[i/128][kb] * sB[j/128][kb]) * P_kb[i][j],
  *   P_kb[i][j] = sum_{k = 128 kb}^{128 kb + 127} dec(A[i][k]) * dec(B[j][k])
  *
- * i.e. every 128-wide K-block's partial product is formed by the FP8 matrix
- * cores with FP32 accumulation and then rescaled in FP32 by that block's A and
- * B scale factors before it is added to the FP32 accumulator.  dec() is the
+ * i.e. every 128-wide K-block's partial product is formed with FP32-grade
+ * accumulation (on gfx950 by the FP16 matrix cores, which represent every
+ * E4M3 value exactly) and then rescaled in FP32 by that block's A and B scale
+ * factors before it is added to the FP32 accumulator.  dec() is the
  * OCP E4M3FN decode: 1 sign, 4 exponent (bias 7), 3 mantissa bits, largest
  * finite value 448 (DeepGEMM FP8 kernel write-up, demingchina.com/news/60142,
  * section 3.1 table).  The result is written once, as FP32 or as BF16
@@ -41,7 +42,7 @@
  *     out_dtype, A / B / C not 16-byte aligned, sA / sB / group_offsets not
  *     4-byte aligned.
  *   - Shapes outside the supported set return DG_ERR_UNSUPPORTED: K must be a
- *     multiple of 128 and N a multiple of 8.  M is arbitrary.
+ *     multiple of 128 and at most 2^22, N a multiple of 8.  M is arbitrary.
  *   - Empty work (M == 0 or N == 0) is a no-op that returns DG_OK.  K == 0
  *     writes zeros.
  *   - A failed kernel launch returns DG_ERR_LAUNCH.  Faults inside a kernel

@@ -5,6 +5,7 @@
 // and the same checks run on a machine without a GPU.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "dg.h"
 #include "gemm_f16mma.hpp"
@@ -12,6 +13,8 @@
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+// Byte offsets inside a 512-row tile are 32-bit: 512 * K < 2^32.
+constexpr int64_t kMaxK = int64_t(1) << 22;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -29,35 +32,47 @@ int check_common(const void* A, const float* sA, const void* B, const float* sB,
       return DG_ERR_INVALID_ARG;
   }
   if (K % dg::KBLK != 0 || N % 8 != 0) return DG_ERR_UNSUPPORTED;
+  if (K > kMaxK) return DG_ERR_UNSUPPORTED;
   return DG_OK;
 }
 
-// Tile shape of one launch.  128 x 256 tiles give each wave a 64 x 128
-// sub-tile (the best operand reuse the register file allows); narrower
-// problems, or ones that would leave most CUs idle, take 128 x 128 tiles.
+// Tile shape of one launch.  Every wave owns a 64 x 128 sub-tile.  The
+// 128 x 512 tile runs 8 waves (two per SIMD, one workgroup per CU, 160 KB of
+// LDS); the 128 x 256 tile runs 4 waves and serves narrow problems.
+// DG_FORCE_TILE=512 or 256 overrides the choice (tuning aid).
 constexpr int kCUs = 256;
 
-template <int BM, int BN>
-int launch_tiles(dg::GemmArgs a, void (*k_bf16)(dg::GemmArgs), void (*k_f32)(dg::GemmArgs),
-                 int out_dtype, hipStream_t stream) {
-  a.m_tiles = int((int64_t(a.M) + BM - 1) / BM);
-  a.n_tiles = int((int64_t(a.N) + BN - 1) / BN);
+int forced_tile() {
+  static const int v = [] {
+    const char* e = getenv("DG_FORCE_TILE");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
+int launch_tiles(dg::GemmArgs a, int bn, int threads, void (*k_bf16)(dg::GemmArgs),
+                 void (*k_f32)(dg::GemmArgs), int out_dtype, hipStream_t stream) {
+  a.m_tiles = int((int64_t(a.M) + 127) / 128);
+  a.n_tiles = int((int64_t(a.N) + bn - 1) / bn);
   const int64_t blocks = int64_t(a.m_tiles) * a.n_tiles;
   if (blocks <= 0) return DG_OK;
   if (blocks > INT32_MAX) return DG_ERR_UNSUPPORTED;
   void* kargs[] = {&a};
   const void* fn = out_dtype == DG_OUT_BF16 ? reinterpret_cast<const void*>(k_bf16)
                                             : reinterpret_cast<const void*>(k_f32);
-  hipError_t err = hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(256), kargs, 0, stream);
+  hipError_t err = hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(threads), kargs, 0, stream);
   return err == hipSuccess ? DG_OK : DG_ERR_LAUNCH;
 }
 
 int launch(const dg::GemmArgs& a, int out_dtype, hipStream_t stream) {
   const int64_t m_tiles = (int64_t(a.M) + 127) / 128;
-  const int64_t wide = m_tiles * ((int64_t(a.N) + 255) / 256);
-  if (a.N > 128 && wide >= kCUs)
-    return launch_tiles<128, 256>(a, dg::dg_gemm_128x256_bf16, dg::dg_gemm_128x256_f32, out_dtype, stream);
-  return launch_tiles<128, 128>(a, dg::dg_gemm_128x128_bf16, dg::dg_gemm_128x128_f32, out_dtype, stream);
+  const int64_t wide = m_tiles * ((int64_t(a.N) + 511) / 512);
+  bool use512 = a.N > 256 && wide >= kCUs / 2;
+  if (forced_tile() == 512) use512 = true;
+  if (forced_tile() == 256) use512 = false;
+  if (use512)
+    return launch_tiles(a, 512, 512, dg::dg_gemm_128x512_bf16, dg::dg_gemm_128x512_f32, out_dtype, stream);
+  return launch_tiles(a, 256, 256, dg::dg_gemm_128x256_bf16, dg::dg_gemm_128x256_f32, out_dtype, stream);
 }
 
 }  // namespace
@@ -109,7 +124,7 @@ const char* dg_status_string(int status) {
   switch (status) {
     case DG_OK: return "DG_OK: success";
     case DG_ERR_INVALID_ARG: return "DG_ERR_INVALID_ARG: invalid argument (null, misaligned, negative or oversized)";
-    case DG_ERR_UNSUPPORTED: return "DG_ERR_UNSUPPORTED: shape not supported (K % 128 != 0 or N % 8 != 0)";
+    case DG_ERR_UNSUPPORTED: return "DG_ERR_UNSUPPORTED: shape not supported (K % 128 != 0, N % 8 != 0 or K > 2^22)";
     case DG_ERR_LAUNCH: return "DG_ERR_LAUNCH: kernel launch failed";
     default: return "unknown dg_status";
   }

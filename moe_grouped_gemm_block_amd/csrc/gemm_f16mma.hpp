@@ -20,21 +20,25 @@
 //
 // Structure (tiling of the DeepGEMM FP8 kernel write-up, demingchina.com/
 // news/60142, sections 2.3 and 3.3-4.3, re-planned for CDNA4):
-//   * one workgroup = 4 waves = a BM x BN tile of C, waves 2 x 2, each wave a
-//     (BM/2) x (BN/2) sub-tile;
+//   * a workgroup of NWM x NWN waves computes a (64 NWM) x (128 NWN) tile of
+//     C; every wave owns a 64 x 128 sub-tile (16 x 16 MFMA tiles 4 x 8).  With
+//     8 waves, two share each SIMD so that one wave's vector work (format
+//     conversion, rescale) overlaps the other's matrix-core work;
 //   * A and B stay FP8 in HBM and LDS.  Each K-block's tiles are copied
-//     straight into LDS with 16-byte global->LDS loads (no VGPR staging), two
-//     stages (double buffering: the next block streams in while the current
-//     one is multiplied);
-//   * inside a 128-byte LDS row, 16-byte granules are XOR-swizzled (see
-//     common.hpp) so fragment reads do not collide on banks;
+//     straight into LDS by bounds-checked buffer loads (16 bytes per lane, no
+//     VGPR staging; rows past the matrix edge read as zeros), two stages:
+//     the next K-block streams in while the current one is multiplied;
+//   * inside a 128-byte LDS row the 16-byte granules are XOR-swizzled with a
+//     pattern that repeats every 16 rows (see swz16), so fragment reads are
+//     spread over the banks and every read of a wave is one base register
+//     plus an immediate offset;
 //   * B rows are permuted on their way into LDS so that, with B as the MFMA's
-//     first operand, every lane ends up holding (BN/8) consecutive columns of
-//     one output row: the epilogue writes whole 16-byte vectors;
+//     first operand, each lane ends up holding 32 consecutive columns of one
+//     output row: the epilogue writes whole 16-byte vectors;
 //   * per K-block and wave: FP8 fragments -> FP16 in registers, 4 chained
-//     16x16x32 FP16 MFMAs per 16x16 output tile give the block partial P,
-//     then acc = fma(sA*sB, P, acc) in FP32.  With 128-row scale blocks and
-//     wave sub-tiles that never straddle them, sA*sB is one scalar per wave;
+//     16x16x32 FP16 MFMAs per 16 x 16 output tile give the block partial P,
+//     then acc = fma(sA*sB, P, acc) in FP32.  Wave sub-tiles never straddle
+//     a 128 x 128 scale block, so sA*sB is one scalar per wave and K-block;
 //   * tiles are ordered so that each XCD (own L2) works on a compact group of
 //     row and column tiles.
 #pragma once
@@ -76,6 +80,21 @@ __device__ __forceinline__ v4f mfma16_f16(const v8h& a, const v8h& b, const v4f&
 // wave's outstanding global->LDS copies.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Swizzle of the 16-byte granule g of LDS row r: slot g ^ f(r) with
+// f(r) = (r & 7) ^ ((r >> 3) & 1).  Within any 16 consecutive rows starting
+// at a multiple of 16, (r & 1, f(r)) takes 16 distinct values, so the 16
+// lanes that read one granule of 16 rows hit 16 distinct 16-byte bank groups
+// of a 256-byte window (and 8 distinct ones per 8 rows); f depends on r mod
+// 16 only.  This is the 8-row XOR swizzle of the DeepGEMM FP8 kernel
+// write-up (section 4.2) re-derived for 16-byte granules and 64-lane reads.
+__device__ __forceinline__ int swz16(int r, int g) { return g ^ ((r & 7) ^ ((r >> 3) & 1)); }
+
+// Raw buffer resource over `bytes` bytes at `base`: loads at offsets
+// >= bytes return zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
 struct GemmArgs {
   const uint8_t* A;       // [M][K]
   const float* sA;        // [ceil(M/128)][K/128]
@@ -106,14 +125,18 @@ __device__ __forceinline__ void tile_of(int bid, int m_tiles, int n_tiles, int& 
   tn = r / gsize;
 }
 
-template <int BM, int BN, bool OUT_BF16>
+template <int NWM, int NWN, bool OUT_BF16>
 __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
-  constexpr int WM = BM / 2, WN = BN / 2;      // wave sub-tile
+  constexpr int WM = 64, WN = 128;             // wave sub-tile
   constexpr int MI = WM / 16, NI = WN / 16;    // 16x16 MFMA tiles per wave
-  constexpr int STAGE = (BM + BN) * KBLK;      // bytes per LDS stage
-  static_assert(BM % 32 == 0 && BN % 64 == 0 && WN <= 128 && WM <= 128, "tile shape");
-  static_assert(WN % 64 == 0 || WN == 32, "column permutation needs WN/4 a multiple of 8");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+  constexpr int NW = NWM * NWN;                // waves per workgroup
+  constexpr int BM = NWM * WM, BN = NWN * WN;  // workgroup tile
+  constexpr int A_BYTES = BM * KBLK, B_BYTES = BN * KBLK;
+  constexpr int A_CH = BM / 8 / NW, B_CH = BN / 8 / NW;   // 1 KB copy chunks per wave
+  static_assert(A_CH * 8 * NW == BM && B_CH * 8 * NW == BN, "chunking");
+  static_assert(NW % 2 == 0, "chunk parity per wave assumes an even wave count");
+  // LDS: [A stage 0][A stage 1][B stage 0][B stage 1]
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (A_BYTES + B_BYTES)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -130,58 +153,51 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
     e = find_group(p.offs, p.G, m0);
     if (e >= p.G) return;                      // uniform across the workgroup
   }
-  const uint8_t* __restrict__ Ag = p.A;
-  const uint8_t* __restrict__ Bg = p.B + (size_t)e * N * K;
-
-  const int wm = (wave >> 1) * WM;             // wave sub-tile origin in the tile
-  const int wn = (wave & 1) * WN;
+  const int wm = (wave / NWN) * WM;            // wave sub-tile origin in the tile
+  const int wn = (wave % NWN) * WN;
   // scale rows of this wave (clamped: a wave wholly past the edge stores nothing)
   const int mb = min((m0 + wm) / KBLK, (M - 1) / KBLK);
   const int nb = min((n0 + wn) / KBLK, Nb - 1);
   const float* __restrict__ sAr = p.sA + (size_t)mb * Kb;
   const float* __restrict__ sBr = p.sB + ((size_t)e * Nb + nb) * Kb;
 
-  // ---- per-lane source rows of the global->LDS copies ----------------------
-  // Chunk c covers LDS rows 8c .. 8c+7 of a tile (1 KB); lane L fills row
-  // 8c + L/8, slot L%8, with global granule (L%8) ^ swizzle(row).
-  constexpr int A_CH = BM / 8 / 4, B_CH = BN / 8 / 4;   // chunks per wave
-  const uint8_t* a_src[A_CH];
-  const uint8_t* b_src[B_CH];
-  int a_dst[A_CH], b_dst[B_CH];
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int c = wave + 4 * i;
-    const int r = 8 * c + (lane >> 3);
-    const int g = (lane & 7) ^ ((r ^ (r >> 3)) & 7);
-    const int gm = min(m0 + r, M - 1);         // rows past M only feed rows that are never stored
-    a_src[i] = Ag + (size_t)gm * K + g * 16;
-    a_dst[i] = 8 * c * KBLK;
-  }
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int c = wave + 4 * i;
-    const int r = 8 * c + (lane >> 3);         // LDS row in the B tile
-    const int half = r / WN, pr = r % WN;      // wave column half, row inside it
-    const int ii = pr % 16, ni = pr / 16;      // MFMA operand row ii of column tile ni
-    const int nl = (ii >> 2) * (WN / 4) + ni * 4 + (ii & 3);
-    const int g = (lane & 7) ^ ((r ^ (r >> 3)) & 7);
-    const int gn = min(n0 + half * WN + nl, N - 1);
-    b_src[i] = Bg + (size_t)gn * K + g * 16;
-    b_dst[i] = BM * KBLK + 8 * c * KBLK;
-  }
+  // ---- global -> LDS copies --------------------------------------------------
+  // Buffer resources start at the tile's first row and end at the matrix
+  // edge, so rows past M (or N) come back as zeros.
+  const __amdgpu_buffer_rsrc_t rA =
+      make_rsrc(p.A + (size_t)m0 * K, uint32_t(min(M - m0, BM)) * uint32_t(K));
+  const __amdgpu_buffer_rsrc_t rB =
+      make_rsrc(p.B + ((size_t)e * N + n0) * K, uint32_t(min(N - n0, BN)) * uint32_t(K));
+  // Chunk c = 1 KB = LDS rows 8c .. 8c+7 of a tile; lane L fills row 8c + L/8,
+  // slot L%8, with granule (L%8) ^ f(row).  This wave copies chunks
+  // c = wave + NW i; all of them have the parity of `wave`, so f(row) =
+  // (L/8) ^ (wave & 1) and one per-lane offset serves every chunk.
+  const int lr = lane >> 3;
+  const int gsl = ((lane & 7) ^ lr ^ (wave & 1)) * 16;
+  const uint32_t a_lane = uint32_t(lr * K + gsl);
+  // B: LDS row r = 8c + L/8 holds, inside column half h = r / 128, operand
+  // row ii = r % 16 of MFMA column tile ni = (r % 128) / 16, i.e. the tile
+  // row 128 h + 32 (ii / 4) + 4 ni + ii % 4.
+  const uint32_t b_lane = uint32_t((32 * (lane >> 5) + (lr & 3)) * K + gsl);
 
   auto issue_copies = [&](int kb, int stage) {
-    uint8_t* base = lds + stage * STAGE;
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i)
-      __builtin_amdgcn_global_load_lds(a_src[i] + (size_t)kb * KBLK,
-                                       (__attribute__((address_space(3))) void*)(base + a_dst[i]),
-                                       16, 0, 0);
+    for (int i = 0; i < A_CH; ++i) {
+      const int c = wave + NW * i;
+      const uint32_t voff = a_lane + uint32_t(8 * c * K + kb * KBLK);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rA, (__attribute__((address_space(3))) void*)(lds + stage * A_BYTES + c * 1024), 16, voff,
+          0, 0, 0);
+    }
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i)
-      __builtin_amdgcn_global_load_lds(b_src[i] + (size_t)kb * KBLK,
-                                       (__attribute__((address_space(3))) void*)(base + b_dst[i]),
-                                       16, 0, 0);
+    for (int i = 0; i < B_CH; ++i) {
+      const int c = wave + NW * i;
+      const int row = 128 * (c >> 4) + 64 * (c & 1) + 4 * ((c & 15) >> 1);
+      const uint32_t voff = b_lane + uint32_t(row * K + kb * KBLK);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rB, (__attribute__((address_space(3))) void*)(lds + 2 * A_BYTES + stage * B_BYTES + c * 1024),
+          16, voff, 0, 0, 0);
+    }
   };
 
   v4f acc[MI][NI];
@@ -192,6 +208,11 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
 
   const int q = lane >> 4;                     // 32-byte K chunk of this lane
   const int r16 = lane & 15;
+  // fragment read offsets (bytes) of this lane inside a tile's wave rows
+  const int a_off0 = (wm + r16) * KBLK + swz16(r16, 2 * q) * 16;
+  const int a_off1 = (wm + r16) * KBLK + swz16(r16, 2 * q + 1) * 16;
+  const int b_off0 = (wn + r16) * KBLK + swz16(r16, 2 * q) * 16;
+  const int b_off1 = (wn + r16) * KBLK + swz16(r16, 2 * q + 1) * 16;
 
   if (Kb > 0) {
     issue_copies(0, 0);
@@ -203,39 +224,40 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
     const int stage = kb & 1;
     if (kb + 1 < Kb) issue_copies(kb + 1, stage ^ 1);
     const float s = sAr[kb] * sBr[kb];
-    const uint8_t* la = lds + stage * STAGE;
-    const uint8_t* lb = la + BM * KBLK;
+    const uint8_t* la = lds + stage * A_BYTES;
+    const uint8_t* lb = lds + 2 * A_BYTES + stage * B_BYTES;
 
     // A fragments (MFMA second operand): rows wm + 16 mi + r16, bytes [32q, 32q+32)
     v8h af[MI][4];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-      const int r = wm + mi * 16 + r16;
-      const int4 x0 = *reinterpret_cast<const int4*>(la + r * KBLK + swz(r, 2 * q) * 16);
-      const int4 x1 = *reinterpret_cast<const int4*>(la + r * KBLK + swz(r, 2 * q + 1) * 16);
+      const int4 x0 = *reinterpret_cast<const int4*>(la + a_off0 + mi * 16 * KBLK);
+      const int4 x1 = *reinterpret_cast<const int4*>(la + a_off1 + mi * 16 * KBLK);
       fp8x32_to_f16(x0, x1, af[mi]);
     }
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
-      const int r = wn + ni * 16 + r16;
-      const int4 y0 = *reinterpret_cast<const int4*>(lb + r * KBLK + swz(r, 2 * q) * 16);
-      const int4 y1 = *reinterpret_cast<const int4*>(lb + r * KBLK + swz(r, 2 * q + 1) * 16);
+      const int4 y0 = *reinterpret_cast<const int4*>(lb + b_off0 + ni * 16 * KBLK);
+      const int4 y1 = *reinterpret_cast<const int4*>(lb + b_off1 + ni * 16 * KBLK);
       v8h bf[4];
       fp8x32_to_f16(y0, y1, bf);
+      v4f part[MI];
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        v4f part = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int mi = 0; mi < MI; ++mi) part[mi] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < 4; ++st) part = mfma16_f16(bf[st], af[mi][st], part);
+      for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[mi][ni][r] = __builtin_fmaf(s, part[r], acc[mi][ni][r]);
-      }
+        for (int mi = 0; mi < MI; ++mi) part[mi] = mfma16_f16(bf[st], af[mi][st], part[mi]);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[mi][ni][r] = __builtin_fmaf(s, part[mi][r], acc[mi][ni][r]);
     }
     wait_vmem();
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds C[m][n0 + wn + q*(WN/4) + 0 .. WN/4-1] --------
+  // ---- epilogue: lane holds C[m][n0 + wn + 32 q + 0 .. 31] ------------------
   constexpr int CW = WN / 4;                   // consecutive columns per lane
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
@@ -273,12 +295,14 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
 }
 
 // Named kernels (one per tile shape and output type) around the body.
-#define DG_GEMM_KERNEL(NAME, BM, BN, BF16) \
-  __global__ __launch_bounds__(256, 1) void NAME(GemmArgs p) { gemm_f16mma_body<BM, BN, BF16>(p); }
-DG_GEMM_KERNEL(dg_gemm_128x256_bf16, 128, 256, true)
-DG_GEMM_KERNEL(dg_gemm_128x256_f32, 128, 256, false)
-DG_GEMM_KERNEL(dg_gemm_128x128_bf16, 128, 128, true)
-DG_GEMM_KERNEL(dg_gemm_128x128_f32, 128, 128, false)
+#define DG_GEMM_KERNEL(NAME, NWM, NWN, BF16)                              \
+  __global__ __launch_bounds__(64 * NWM * NWN, 1) void NAME(GemmArgs p) { \
+    gemm_f16mma_body<NWM, NWN, BF16>(p);                                  \
+  }
+DG_GEMM_KERNEL(dg_gemm_128x512_bf16, 2, 4, true)
+DG_GEMM_KERNEL(dg_gemm_128x512_f32, 2, 4, false)
+DG_GEMM_KERNEL(dg_gemm_128x256_bf16, 2, 2, true)
+DG_GEMM_KERNEL(dg_gemm_128x256_f32, 2, 2, false)
 #undef DG_GEMM_KERNEL
 
 }  // namespace dg
