@@ -76,6 +76,19 @@ __device__ __forceinline__ v4f mfma16_f16(const v8h& a, const v8h& b, const v4f&
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Returns x unchanged through an empty (non-volatile) asm, which the
+// optimiser cannot see through: used on per-K-block copy offsets so that they
+// are not strength-reduced into one long-lived register per copy chunk.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm("" : "+v"(x));
+  return x;
+}
+
+// Lane index recomputed on the spot (keeps it from living across the K loop).
+__device__ __forceinline__ int lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
 // s_waitcnt vmcnt(0) (expcnt / lgkmcnt left at their maxima): waits for this
 // wave's outstanding global->LDS copies.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -89,10 +102,29 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // write-up (section 4.2) re-derived for 16-byte granules and 64-lane reads.
 __device__ __forceinline__ int swz16(int r, int g) { return g ^ ((r & 7) ^ ((r >> 3) & 1)); }
 
-// Raw buffer resource over `bytes` bytes at `base`: loads at offsets
-// >= bytes return zeros instead of touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (stride 0) over `bytes` bytes at `base`: loads at
+// offsets >= bytes return zeros instead of touching memory.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = int(uint32_t(a));
+  r[1] = int(uint32_t(a >> 32) & 0xffffu);   // stride 0
+  r[2] = int(bytes);                          // num_records
+  r[3] = 0x00020000;                          // 32-bit data format
+  return r;
+}
+
+// 16 bytes per lane from buffer `rsrc` at byte offset `voff` straight into
+// LDS at `lds_base` + 16 * lane (lds_base is wave-uniform, passed in M0).
+// Written as inline assembly on purpose: the compiler then does not treat
+// the copy as an LDS store that every later LDS read must wait for -- the
+// copies always target the stage that is not being read, and the kernel
+// waits for them itself (s_waitcnt vmcnt(0) + barrier) before switching.
+__device__ __forceinline__ void copy16_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t lds_base) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_base)
+               : "memory");
 }
 
 struct GemmArgs {
@@ -158,16 +190,17 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   // scale rows of this wave (clamped: a wave wholly past the edge stores nothing)
   const int mb = min((m0 + wm) / KBLK, (M - 1) / KBLK);
   const int nb = min((n0 + wn) / KBLK, Nb - 1);
-  const float* __restrict__ sAr = p.sA + (size_t)mb * Kb;
-  const float* __restrict__ sBr = p.sB + ((size_t)e * Nb + nb) * Kb;
+  // Scales are read through the constant address space so that they become
+  // scalar loads (counted apart from the vector-memory copies into LDS).
+  typedef const __attribute__((address_space(4))) float cfloat;
+  cfloat* sAr = (cfloat*)(p.sA + (size_t)mb * Kb);
+  cfloat* sBr = (cfloat*)(p.sB + ((size_t)e * Nb + nb) * Kb);
 
   // ---- global -> LDS copies --------------------------------------------------
   // Buffer resources start at the tile's first row and end at the matrix
   // edge, so rows past M (or N) come back as zeros.
-  const __amdgpu_buffer_rsrc_t rA =
-      make_rsrc(p.A + (size_t)m0 * K, uint32_t(min(M - m0, BM)) * uint32_t(K));
-  const __amdgpu_buffer_rsrc_t rB =
-      make_rsrc(p.B + ((size_t)e * N + n0) * K, uint32_t(min(N - n0, BN)) * uint32_t(K));
+  const i32x4 rA = make_rsrc(p.A + (size_t)m0 * K, uint32_t(min(M - m0, BM)) * uint32_t(K));
+  const i32x4 rB = make_rsrc(p.B + ((size_t)e * N + n0) * K, uint32_t(min(N - n0, BN)) * uint32_t(K));
   // Chunk c = 1 KB = LDS rows 8c .. 8c+7 of a tile; lane L fills row 8c + L/8,
   // slot L%8, with granule (L%8) ^ f(row).  This wave copies chunks
   // c = wave + NW i; all of them have the parity of `wave`, so f(row) =
@@ -180,23 +213,24 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   // row 128 h + 32 (ii / 4) + 4 ni + ii % 4.
   const uint32_t b_lane = uint32_t((32 * (lane >> 5) + (lr & 3)) * K + gsl);
 
+  // LDS byte address of the buffer (wave-uniform)
+  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
+      uint32_t(reinterpret_cast<uintptr_t>(static_cast<void*>(lds))));
   auto issue_copies = [&](int kb, int stage) {
+    const uint32_t a_kb = opaque(a_lane + uint32_t(kb * KBLK));
+    const uint32_t b_kb = opaque(b_lane + uint32_t(kb * KBLK));
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int c = wave + NW * i;
-      const uint32_t voff = a_lane + uint32_t(8 * c * K + kb * KBLK);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rA, (__attribute__((address_space(3))) void*)(lds + stage * A_BYTES + c * 1024), 16, voff,
-          0, 0, 0);
+      const uint32_t voff = a_kb + uint32_t(8 * c * K);
+      copy16_to_lds(rA, voff, lds_addr + uint32_t(stage * A_BYTES + c * 1024));
     }
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       const int c = wave + NW * i;
       const int row = 128 * (c >> 4) + 64 * (c & 1) + 4 * ((c & 15) >> 1);
-      const uint32_t voff = b_lane + uint32_t(row * K + kb * KBLK);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rB, (__attribute__((address_space(3))) void*)(lds + 2 * A_BYTES + stage * B_BYTES + c * 1024),
-          16, voff, 0, 0, 0);
+      const uint32_t voff = b_kb + uint32_t(row * K);
+      copy16_to_lds(rB, voff, lds_addr + uint32_t(2 * A_BYTES + stage * B_BYTES + c * 1024));
     }
   };
 
@@ -220,10 +254,15 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
     __syncthreads();
   }
 
+  float sa_next = Kb > 0 ? sAr[0] : 0.f, sb_next = Kb > 0 ? sBr[0] : 0.f;
   for (int kb = 0; kb < Kb; ++kb) {
     const int stage = kb & 1;
-    if (kb + 1 < Kb) issue_copies(kb + 1, stage ^ 1);
-    const float s = sAr[kb] * sBr[kb];
+    const float s = sa_next * sb_next;         // this K-block's fp32(sA * sB)
+    if (kb + 1 < Kb) {
+      sa_next = sAr[kb + 1];                   // prefetched one K-block ahead
+      sb_next = sBr[kb + 1];
+      issue_copies(kb + 1, stage ^ 1);
+    }
     const uint8_t* la = lds + stage * A_BYTES;
     const uint8_t* lb = lds + 2 * A_BYTES + stage * B_BYTES;
 
@@ -235,35 +274,89 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
       const int4 x1 = *reinterpret_cast<const int4*>(la + a_off1 + mi * 16 * KBLK);
       fp8x32_to_f16(x0, x1, af[mi]);
     }
+    // B column tiles, software-pipelined: while the MFMAs of tile ni consume
+    // operand st, operand st of tile ni+1 is converted into the registers
+    // they free, and the FP32 rescale of tile ni-1 is threaded between the
+    // first MFMAs of tile ni.  Raw FP8 of tile ni+2 is read from LDS one tile
+    // ahead.
+    int4 y0 = *reinterpret_cast<const int4*>(lb + b_off0);
+    int4 y1 = *reinterpret_cast<const int4*>(lb + b_off1);
+    v8h bf[4];
+    fp8x32_to_f16(y0, y1, bf);
+    if (NI > 1) {
+      y0 = *reinterpret_cast<const int4*>(lb + b_off0 + 16 * KBLK);
+      y1 = *reinterpret_cast<const int4*>(lb + b_off1 + 16 * KBLK);
+    }
+    v4f part[MI];
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
-      const int4 y0 = *reinterpret_cast<const int4*>(lb + b_off0 + ni * 16 * KBLK);
-      const int4 y1 = *reinterpret_cast<const int4*>(lb + b_off1 + ni * 16 * KBLK);
-      v8h bf[4];
-      fp8x32_to_f16(y0, y1, bf);
-      v4f part[MI];
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) part[mi] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int st = 0; st < 4; ++st) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
+        for (int mi = 0; mi < MI; ++mi) {
+          if (st == 0 && ni > 0) {
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) part[mi] = mfma16_f16(bf[st], af[mi][st], part[mi]);
+            for (int r = 0; r < 4; ++r)
+              acc[mi][ni - 1][r] = __builtin_fmaf(s, part[mi][r], acc[mi][ni - 1][r]);
+          }
+          part[mi] = mfma16_f16(bf[st], af[mi][st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : part[mi]);
+        }
+        if (ni + 1 < NI) {
+          // operand st of tile ni+1: raw dwords 2st, 2st+1
+          const int4& y = st < 2 ? y0 : y1;
+          const uint32_t w0 = uint32_t((st & 1) ? y.z : y.x), w1 = uint32_t((st & 1) ? y.w : y.y);
+          uint32_t h[4];
+          fp8x4_to_f16(w0, h[0], h[1]);
+          fp8x4_to_f16(w1, h[2], h[3]);
+          bf[st] = __builtin_bit_cast(v8h, (uint4{h[0], h[1], h[2], h[3]}));
+          if (ni + 2 < NI && st == 1)
+            y0 = *reinterpret_cast<const int4*>(lb + b_off0 + (ni + 2) * 16 * KBLK);
+          if (ni + 2 < NI && st == 3)
+            y1 = *reinterpret_cast<const int4*>(lb + b_off1 + (ni + 2) * 16 * KBLK);
+        }
+      }
+      // pin the interleave: rescale / MFMA alternation, then MFMA / convert
+      if (ni > 0) {
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+        for (int mi = 0; mi < MI; ++mi) {
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU (rescale)
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+        }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
+      if (ni + 1 < NI) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[mi][ni][r] = __builtin_fmaf(s, part[mi][r], acc[mi][ni][r]);
+        for (int st = 0; st < 4; ++st) {
+          if (st > 0) {
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+              __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // 1 VALU (convert)
+            }
+          } else {
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);     // converts of operand 0
+          }
+        }
+      }
     }
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[mi][NI - 1][r] = __builtin_fmaf(s, part[mi][r], acc[mi][NI - 1][r]);
     wait_vmem();
     __syncthreads();
   }
 
   // ---- epilogue: lane holds C[m][n0 + wn + 32 q + 0 .. 31] ------------------
   constexpr int CW = WN / 4;                   // consecutive columns per lane
+  const int lane_e = lane_id();
+  const int q_e = lane_e >> 4, r16_e = lane_e & 15;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
-    const int m = m0 + wm + mi * 16 + r16;
+    const int m = m0 + wm + mi * 16 + r16_e;
     if (m >= M) continue;
-    const int nbase = n0 + wn + q * CW;
+    const int nbase = n0 + wn + q_e * CW;
     float v[CW];
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
