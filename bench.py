@@ -43,6 +43,16 @@ INFINITY_CACHE = 256 << 20
 HBM_BOUND = {3, 5}           # workloads whose roofline is HBM bandwidth
 
 
+def gemm_tflops(M: int, N: int, K: int, seconds: float) -> float:
+    """Algorithmic throughput of an M x N x K GEMM: 2 M N K FLOP / time."""
+    return 2.0 * M * N * K / seconds / 1e12
+
+
+def intensity(M: int, N: int, K: int, elem_bytes: float) -> float:
+    """FLOP per byte when A, B and C each cross memory once."""
+    return 2.0 * M * N * K / ((M * K + K * N + M * N) * elem_bytes)
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -213,7 +223,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
     else:
-        achieved = flop / (kern_ms * 1e-3) / 1e12
+        achieved = flop / (kern_ms * 1e-3) / 1e12   # == gemm_tflops for dense problems
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4)}
     roof["traffic"] = measured_traffic(p.name)

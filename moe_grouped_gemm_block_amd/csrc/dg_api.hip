@@ -9,6 +9,7 @@
 
 #include "dg.h"
 #include "gemm_f16mma.hpp"
+#include "gemm_skinny.hpp"
 
 namespace {
 
@@ -64,7 +65,28 @@ int launch_tiles(dg::GemmArgs a, int bn, int threads, void (*k_bf16)(dg::GemmArg
   return err == hipSuccess ? DG_OK : DG_ERR_LAUNCH;
 }
 
+// Few rows (M <= 64, dense): one workgroup per 16*NI columns, its four waves
+// splitting K; NI = 3 once that still gives every CU a workgroup.
+int launch_skinny(dg::GemmArgs a, int out_dtype, hipStream_t stream) {
+  typedef void (*kfn)(dg::GemmArgs);
+  // [rows 16/32/64][NI 1/3][f32/bf16]
+  static const kfn table[3][2][2] = {
+      {{dg::dg_skinny_m16_n16_f32, dg::dg_skinny_m16_n16_bf16}, {dg::dg_skinny_m16_n48_f32, dg::dg_skinny_m16_n48_bf16}},
+      {{dg::dg_skinny_m32_n16_f32, dg::dg_skinny_m32_n16_bf16}, {dg::dg_skinny_m32_n48_f32, dg::dg_skinny_m32_n48_bf16}},
+      {{dg::dg_skinny_m64_n16_f32, dg::dg_skinny_m64_n16_bf16}, {dg::dg_skinny_m64_n48_f32, dg::dg_skinny_m64_n48_bf16}}};
+  const int rows = a.M <= 16 ? 0 : a.M <= 32 ? 1 : 2;
+  const int wide = int64_t(a.N) >= int64_t(48) * kCUs ? 1 : 0;
+  const int cols = wide ? 48 : 16;
+  const int64_t blocks = (int64_t(a.N) + cols - 1) / cols;
+  if (blocks > INT32_MAX) return DG_ERR_UNSUPPORTED;
+  void* kargs[] = {&a};
+  const void* fn = reinterpret_cast<const void*>(table[rows][wide][out_dtype == DG_OUT_BF16 ? 1 : 0]);
+  hipError_t err = hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(256), kargs, 0, stream);
+  return err == hipSuccess ? DG_OK : DG_ERR_LAUNCH;
+}
+
 int launch(const dg::GemmArgs& a, int out_dtype, hipStream_t stream) {
+  if (a.offs == nullptr && a.M <= 64 && forced_tile() == 0) return launch_skinny(a, out_dtype, stream);
   const int64_t m_tiles = (int64_t(a.M) + 127) / 128;
   const int64_t wide = m_tiles * ((int64_t(a.N) + 511) / 512);
   bool use512 = a.N > 256 && wide >= kCUs / 2;

@@ -1,0 +1,192 @@
+// Block-scaled FP8 GEMM for few rows (M <= 64, decode-style shapes), gfx950.
+//
+// Same arithmetic as the tiled kernel (exact FP8 -> FP16 conversion, FP16
+// MFMA partial per 128-wide K-block, FP32 rescale by fp32(sA * sB), FP32
+// accumulation; DeepGEMM FP8-for-MoE page, 2kiu.com/news/5461879, sections 2.1
+// and 3.3), organised for a shape whose cost is streaming B once from HBM:
+// with M = 64, every byte of B feeds only 128 FLOP.
+//
+//   * one workgroup per 16*NI columns of C (all rows); its 4 waves split the
+//     K-blocks (wave w takes kb = w, w+4, ...), so each wave streams distinct
+//     data and needs no barrier inside the K loop;
+//   * every wave copies its own K-blocks (all 16*MI rows of A, 16*NI rows of
+//     B) straight into a private two-stage LDS region with bounds-checked
+//     buffer->LDS loads and waits for them with its own vmcnt -- one K-block
+//     always in flight per wave, four per CU;
+//   * the four per-wave partial sums are added through LDS in a fixed order
+//     (wave 0 + 1 + 2 + 3) before the single rounding to BF16 / FP32, so the
+//     result is bitwise repeatable.
+#pragma once
+
+#include "gemm_f16mma.hpp"
+
+namespace dg {
+
+// s_waitcnt vmcnt(n) with expcnt / lgkmcnt at their maxima (n < 64).
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
+}
+
+template <int MI, int NI, bool OUT_BF16>
+__device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p) {
+  constexpr int NW = 4;                         // waves, each a quarter of the K-blocks
+  constexpr int RM = 16 * MI, CN = 16 * NI;     // rows / columns of the workgroup tile
+  constexpr int A_BYTES = RM * KBLK, B_BYTES = CN * KBLK;
+  constexpr int STAGE = A_BYTES + B_BYTES;      // one K-block of one wave
+  constexpr int A_CH = RM / 8, B_CH = CN / 8;   // 1 KB copy chunks per K-block
+  constexpr int RED = NW * RM * CN * 4;         // partial sums for the reduction
+  constexpr int LDS_BYTES = (NW * 2 * STAGE > RED) ? NW * 2 * STAGE : RED;
+  static_assert(A_CH + B_CH < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * CN;
+  const int M = p.M, N = p.N, K = p.K;
+  const int Kb = K / KBLK;
+  const int Nb = (N + KBLK - 1) / KBLK;
+
+  typedef const __attribute__((address_space(4))) float cfloat;
+  cfloat* sAr = (cfloat*)(p.sA);                // M <= 64: one row block
+  int nbk[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) nbk[ni] = min((n0 + 16 * ni) / KBLK, Nb - 1);
+
+  const i32x4 rA = make_rsrc(p.A, uint32_t(M) * uint32_t(K));
+  const i32x4 rB = make_rsrc(p.B + (size_t)n0 * K, uint32_t(min(N - n0, CN)) * uint32_t(K));
+  // chunk c: LDS rows 8c .. 8c+7; lane L fills row 8c + L/8 slot L%8 with
+  // granule (L%8) ^ f(row), f(row) = (L/8) ^ (c & 1)  (see swz16)
+  const int lr = lane >> 3;
+  const uint32_t lane_even = uint32_t(lr * K + (((lane & 7) ^ lr) * 16));
+  const uint32_t lane_odd = uint32_t(lr * K + (((lane & 7) ^ lr ^ 1) * 16));
+  const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(
+      uint32_t(reinterpret_cast<uintptr_t>(static_cast<void*>(lds))) + uint32_t(wave * 2 * STAGE));
+
+  auto issue = [&](int kb, int stage) {
+    const uint32_t ev = opaque(lane_even + uint32_t(kb * KBLK));
+    const uint32_t od = opaque(lane_odd + uint32_t(kb * KBLK));
+    const uint32_t base = lds_wave + uint32_t(stage * STAGE);
+#pragma unroll
+    for (int c = 0; c < A_CH; ++c)
+      copy16_to_lds(rA, ((c & 1) ? od : ev) + uint32_t(8 * c * K), base + uint32_t(c * 1024));
+#pragma unroll
+    for (int c = 0; c < B_CH; ++c)
+      copy16_to_lds(rB, ((c & 1) ? od : ev) + uint32_t(8 * c * K), base + uint32_t(A_BYTES + c * 1024));
+  };
+
+  v4f acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int q = lane >> 4, r16 = lane & 15;
+  const int off0 = r16 * KBLK + swz16(r16, 2 * q) * 16;
+  const int off1 = r16 * KBLK + swz16(r16, 2 * q + 1) * 16;
+  const uint8_t* lw = lds + wave * 2 * STAGE;
+
+  int j = 0;
+  if (wave < Kb) issue(wave, 0);
+  for (int kb = wave; kb < Kb; kb += NW, ++j) {
+    const int stage = j & 1;
+    float sa = sAr[kb];
+    float sb[NI];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) sb[ni] = ((cfloat*)p.sB)[(size_t)nbk[ni] * Kb + kb];
+    if (kb + NW < Kb) {
+      issue(kb + NW, stage ^ 1);
+      wait_vmem_n<A_CH + B_CH>();               // this K-block landed, the next one in flight
+    } else {
+      wait_vmem_n<0>();
+    }
+    const uint8_t* la = lw + stage * STAGE;
+    const uint8_t* lb = la + A_BYTES;
+    v8h af[MI][4];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int4 x0 = *reinterpret_cast<const int4*>(la + off0 + mi * 16 * KBLK);
+      const int4 x1 = *reinterpret_cast<const int4*>(la + off1 + mi * 16 * KBLK);
+      fp8x32_to_f16(x0, x1, af[mi]);
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int4 y0 = *reinterpret_cast<const int4*>(lb + off0 + ni * 16 * KBLK);
+      const int4 y1 = *reinterpret_cast<const int4*>(lb + off1 + ni * 16 * KBLK);
+      v8h bf[4];
+      fp8x32_to_f16(y0, y1, bf);
+      const float s = sa * sb[ni];
+      v4f part[MI];
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+          part[mi] = mfma16_f16(bf[st], af[mi][st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : part[mi]);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[mi][ni][r] = __builtin_fmaf(s, part[mi][r], acc[mi][ni][r]);
+    }
+  }
+
+  // ---- fixed-order reduction of the four partial sums ----------------------
+  __syncthreads();                              // every wave is done with its stages
+  float* red = reinterpret_cast<float*>(lds);   // [wave][RM][CN]
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      // lane holds rows mi*16 + r16, columns ni*16 + 4q + 0..3
+      float* dst = red + (wave * RM + mi * 16 + r16) * CN + ni * 16 + 4 * q;
+      *reinterpret_cast<float4*>(dst) = float4{acc[mi][ni][0], acc[mi][ni][1], acc[mi][ni][2], acc[mi][ni][3]};
+    }
+  __syncthreads();
+  constexpr int CH8 = CN / 8;                   // 8-column chunks per row
+  for (int c = threadIdx.x; c < RM * CH8; c += 64 * NW) {
+    const int m = c / CH8, n8 = (c % CH8) * 8;
+    const int n = n0 + n8;
+    if (m >= M || n >= N) continue;             // N % 8 == 0: whole chunk in range
+    float v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float* src = red + (w * RM + m) * CN + n8;
+      const float4 a = *reinterpret_cast<const float4*>(src);
+      const float4 b = *reinterpret_cast<const float4*>(src + 4);
+      v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+      v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+    }
+    if constexpr (OUT_BF16) {
+      uint4 w4;
+      w4.x = pack_bf16x2(v[0], v[1]);
+      w4.y = pack_bf16x2(v[2], v[3]);
+      w4.z = pack_bf16x2(v[4], v[5]);
+      w4.w = pack_bf16x2(v[6], v[7]);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.C) + (size_t)m * N + n) = w4;
+    } else {
+      float* row = reinterpret_cast<float*>(p.C) + (size_t)m * N + n;
+      *reinterpret_cast<float4*>(row) = float4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<float4*>(row + 4) = float4{v[4], v[5], v[6], v[7]};
+    }
+  }
+}
+
+#define DG_SKINNY_KERNEL(NAME, MI, NI, BF16) \
+  __global__ __launch_bounds__(256, 1) void NAME(GemmArgs p) { gemm_skinny_body<MI, NI, BF16>(p); }
+DG_SKINNY_KERNEL(dg_skinny_m64_n48_bf16, 4, 3, true)
+DG_SKINNY_KERNEL(dg_skinny_m64_n48_f32, 4, 3, false)
+DG_SKINNY_KERNEL(dg_skinny_m64_n16_bf16, 4, 1, true)
+DG_SKINNY_KERNEL(dg_skinny_m64_n16_f32, 4, 1, false)
+DG_SKINNY_KERNEL(dg_skinny_m32_n48_bf16, 2, 3, true)
+DG_SKINNY_KERNEL(dg_skinny_m32_n48_f32, 2, 3, false)
+DG_SKINNY_KERNEL(dg_skinny_m32_n16_bf16, 2, 1, true)
+DG_SKINNY_KERNEL(dg_skinny_m32_n16_f32, 2, 1, false)
+DG_SKINNY_KERNEL(dg_skinny_m16_n48_bf16, 1, 3, true)
+DG_SKINNY_KERNEL(dg_skinny_m16_n48_f32, 1, 3, false)
+DG_SKINNY_KERNEL(dg_skinny_m16_n16_bf16, 1, 1, true)
+DG_SKINNY_KERNEL(dg_skinny_m16_n16_f32, 1, 1, false)
+#undef DG_SKINNY_KERNEL
+
+}  // namespace dg

@@ -95,6 +95,22 @@ def test_dense_small_full(M, N, K, out):
     check(p, as64(run(p)), what=f"{M}x{N}x{K} {out}")
 
 
+# M <= 64 takes the few-rows kernel: rows not a multiple of 16, a partial last
+# 48-column slab (N = 48*256 + 16), and K-block counts not divisible by the
+# four-way K split (Kb = 1, 3, 5).
+SKINNY = [(1, 12304, 128), (17, 12304, 384), (32, 12288, 640), (48, 520, 256), (64, 12304, 384),
+          (16, 264, 128), (33, 136, 640)]
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", SKINNY)
+def test_skinny_full(M, N, K, out):
+    log(f"skinny M={M} N={N} K={K} out={out}")
+    p = I.dense_problem(M, N, K, seed=M + 3 * N + K, out_dtype=out, block_log2_range=3.0,
+                        outlier_frac=0.01)
+    check(p, as64(run(p)), what=f"skinny {M}x{N}x{K} {out}")
+
+
 def test_config1_full():
     p = I.make_config(1)
     log("workload 1 (256^3, f32)")
