@@ -10,9 +10,10 @@
 //     K-blocks (wave w takes kb = w, w+4, ...), so each wave streams distinct
 //     data and needs no barrier inside the K loop;
 //   * every wave copies its own K-blocks (all 16*MI rows of A, 16*NI rows of
-//     B) straight into a private two-stage LDS region with bounds-checked
-//     buffer->LDS loads and waits for them with its own vmcnt -- one K-block
-//     always in flight per wave, four per CU;
+//     B) straight into a private LDS region with bounds-checked buffer->LDS
+//     loads and waits for them with its own vmcnt.  B, the bytes that come
+//     from HBM, runs two K-blocks ahead (three stages); A, which every
+//     workgroup re-reads from L2, runs one ahead (two stages);
 //   * the four per-wave partial sums are added through LDS in a fixed order
 //     (wave 0 + 1 + 2 + 3) before the single rounding to BF16 / FP32, so the
 //     result is bitwise repeatable.
@@ -34,11 +35,11 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p) {
   constexpr int NW = 4;                         // waves, each a quarter of the K-blocks
   constexpr int RM = 16 * MI, CN = 16 * NI;     // rows / columns of the workgroup tile
   constexpr int A_BYTES = RM * KBLK, B_BYTES = CN * KBLK;
-  constexpr int STAGE = A_BYTES + B_BYTES;      // one K-block of one wave
+  constexpr int WAVE_LDS = 2 * A_BYTES + 3 * B_BYTES;   // A: 2 stages, B: 3 stages
   constexpr int A_CH = RM / 8, B_CH = CN / 8;   // 1 KB copy chunks per K-block
   constexpr int RED = NW * RM * CN * 4;         // partial sums for the reduction
-  constexpr int LDS_BYTES = (NW * 2 * STAGE > RED) ? NW * 2 * STAGE : RED;
-  static_assert(A_CH + B_CH < 64, "vmcnt range");
+  constexpr int LDS_BYTES = (NW * WAVE_LDS > RED) ? NW * WAVE_LDS : RED;
+  static_assert(2 * B_CH + A_CH < 64, "vmcnt range");
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
 
   const int lane = threadIdx.x & 63;
@@ -62,18 +63,24 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p) {
   const uint32_t lane_even = uint32_t(lr * K + (((lane & 7) ^ lr) * 16));
   const uint32_t lane_odd = uint32_t(lr * K + (((lane & 7) ^ lr ^ 1) * 16));
   const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(
-      uint32_t(reinterpret_cast<uintptr_t>(static_cast<void*>(lds))) + uint32_t(wave * 2 * STAGE));
+      uint32_t(reinterpret_cast<uintptr_t>(static_cast<void*>(lds))) + uint32_t(wave * WAVE_LDS));
 
-  auto issue = [&](int kb, int stage) {
+  // wave LDS: [A stage 0][A stage 1][B stage 0][B stage 1][B stage 2]
+  auto issue_a = [&](int kb, int stage) {
     const uint32_t ev = opaque(lane_even + uint32_t(kb * KBLK));
     const uint32_t od = opaque(lane_odd + uint32_t(kb * KBLK));
-    const uint32_t base = lds_wave + uint32_t(stage * STAGE);
+    const uint32_t base = lds_wave + uint32_t(stage * A_BYTES);
 #pragma unroll
     for (int c = 0; c < A_CH; ++c)
       copy16_to_lds(rA, ((c & 1) ? od : ev) + uint32_t(8 * c * K), base + uint32_t(c * 1024));
+  };
+  auto issue_b = [&](int kb, int stage) {
+    const uint32_t ev = opaque(lane_even + uint32_t(kb * KBLK));
+    const uint32_t od = opaque(lane_odd + uint32_t(kb * KBLK));
+    const uint32_t base = lds_wave + uint32_t(2 * A_BYTES + stage * B_BYTES);
 #pragma unroll
     for (int c = 0; c < B_CH; ++c)
-      copy16_to_lds(rB, ((c & 1) ? od : ev) + uint32_t(8 * c * K), base + uint32_t(A_BYTES + c * 1024));
+      copy16_to_lds(rB, ((c & 1) ? od : ev) + uint32_t(8 * c * K), base + uint32_t(c * 1024));
   };
 
   v4f acc[MI][NI];
@@ -85,24 +92,34 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p) {
   const int q = lane >> 4, r16 = lane & 15;
   const int off0 = r16 * KBLK + swz16(r16, 2 * q) * 16;
   const int off1 = r16 * KBLK + swz16(r16, 2 * q + 1) * 16;
-  const uint8_t* lw = lds + wave * 2 * STAGE;
+  const uint8_t* lw = lds + wave * WAVE_LDS;
 
-  int j = 0;
-  if (wave < Kb) issue(wave, 0);
+  // Issue order per iteration j (K-block kb_j = wave + 4j): A(kb_{j+1}) then
+  // B(kb_{j+2}).  A(kb_j) and B(kb_j) are complete once at most
+  // B(kb_{j+1}) + A(kb_{j+1}) + B(kb_{j+2}) copies are still outstanding.
+  int j = 0, bstage = 0;
+  if (wave < Kb) {
+    issue_a(wave, 0);
+    issue_b(wave, 0);
+    if (wave + NW < Kb) issue_b(wave + NW, 1);
+  }
   for (int kb = wave; kb < Kb; kb += NW, ++j) {
-    const int stage = j & 1;
+    const int astage = j & 1;
     float sa = sAr[kb];
     float sb[NI];
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) sb[ni] = ((cfloat*)p.sB)[(size_t)nbk[ni] * Kb + kb];
-    if (kb + NW < Kb) {
-      issue(kb + NW, stage ^ 1);
-      wait_vmem_n<A_CH + B_CH>();               // this K-block landed, the next one in flight
+    if (kb + 2 * NW < Kb) {
+      issue_a(kb + NW, astage ^ 1);
+      issue_b(kb + 2 * NW, bstage == 0 ? 2 : bstage - 1);
+      wait_vmem_n<2 * B_CH + A_CH>();
     } else {
+      if (kb + NW < Kb) issue_a(kb + NW, astage ^ 1);
       wait_vmem_n<0>();
     }
-    const uint8_t* la = lw + stage * STAGE;
-    const uint8_t* lb = la + A_BYTES;
+    const uint8_t* la = lw + astage * A_BYTES;
+    const uint8_t* lb = lw + 2 * A_BYTES + bstage * B_BYTES;
+    bstage = bstage == 2 ? 0 : bstage + 1;
     v8h af[MI][4];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
