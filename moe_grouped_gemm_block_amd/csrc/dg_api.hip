@@ -10,6 +10,7 @@
 #include "dg.h"
 #include "gemm_f16mma.hpp"
 #include "gemm_skinny.hpp"
+#include "gemm_wide.hpp"
 
 namespace {
 
@@ -40,7 +41,8 @@ int check_common(const void* A, const float* sA, const void* B, const float* sB,
 // Tile shape of one launch.  Every wave owns a 64 x 128 sub-tile.  The
 // 128 x 512 tile runs 8 waves (two per SIMD, one workgroup per CU, 160 KB of
 // LDS); the 128 x 256 tile runs 4 waves and serves narrow problems.
-// DG_FORCE_TILE=512 or 256 overrides the choice (tuning aid).
+// DG_FORCE_TILE=512 or 256 overrides the choice, 1512 selects the 1 x 8
+// wave arrangement (tuning aids).
 constexpr int kCUs = 256;
 
 int forced_tile() {
@@ -92,6 +94,9 @@ int launch(const dg::GemmArgs& a, int out_dtype, hipStream_t stream) {
   bool use512 = a.N > 256 && wide >= kCUs / 2;
   if (forced_tile() == 512) use512 = true;
   if (forced_tile() == 256) use512 = false;
+  if (forced_tile() == 1512)
+    return launch_tiles(a, 512, 512, dg::dg_gemm_wide_128x512_bf16, dg::dg_gemm_wide_128x512_f32, out_dtype,
+                        stream);
   if (use512)
     return launch_tiles(a, 512, 512, dg::dg_gemm_128x512_bf16, dg::dg_gemm_128x512_f32, out_dtype, stream);
   return launch_tiles(a, 256, 256, dg::dg_gemm_128x256_bf16, dg::dg_gemm_128x256_f32, out_dtype, stream);

@@ -93,6 +93,13 @@ __device__ __forceinline__ int lane_id() {
 // wave's outstanding global->LDS copies.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt vmcnt(n) with expcnt / lgkmcnt at their maxima (n < 64).
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // Swizzle of the 16-byte granule g of LDS row r: slot g ^ f(r) with
 // f(r) = (r & 7) ^ ((r >> 3) & 1).  Within any 16 consecutive rows starting
 // at a multiple of 16, (r & 1, f(r)) takes 16 distinct values, so the 16
@@ -106,13 +113,14 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Raw buffer resource (stride 0) over `bytes` bytes at `base`: loads at
 // offsets >= bytes return zeros instead of touching memory.
+// Every field goes through readfirstlane: the descriptor must sit in SGPRs.
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   i32x4 r;
-  r[0] = int(uint32_t(a));
-  r[1] = int(uint32_t(a >> 32) & 0xffffu);   // stride 0
-  r[2] = int(bytes);                          // num_records
-  r[3] = 0x00020000;                          // 32-bit data format
+  r[0] = __builtin_amdgcn_readfirstlane(int(uint32_t(a)));
+  r[1] = __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffffu));   // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(int(bytes));                          // num_records
+  r[3] = 0x00020000;                                                          // 32-bit data format
   return r;
 }
 
@@ -140,14 +148,18 @@ struct GemmArgs {
 };
 
 // Tile order: blockIdx -> (m-tile, n-tile).  Workgroups are dealt to the 8
-// XCDs round-robin; consecutive "local" indices on one XCD walk a group of
-// GROUP_M row tiles column by column, so the tiles that run together on an
-// XCD share A rows and B columns in its L2.
+// XCDs round-robin (block b runs on XCD b % 8), so block b is given tile t
+// from a contiguous range per XCD: XCD x owns tiles [start_x, start_x +
+// count_x), the first T % 8 XCDs one tile more than the others.  Inside the
+// range, tiles walk a group of GROUP_M row tiles column by column, so the
+// tiles that run together on one XCD share A rows and B columns in its L2
+// (and, for grouped problems, the same experts' weights).
 template <int GROUP_M>
 __device__ __forceinline__ void tile_of(int bid, int m_tiles, int n_tiles, int& tm, int& tn) {
   const int T = m_tiles * n_tiles;
-  int t = bid;
-  if ((T & 7) == 0) t = (bid & 7) * (T >> 3) + (bid >> 3);
+  const int xcd = bid & 7, local = bid >> 3;
+  const int base = T >> 3, extra = T & 7;
+  const int t = xcd < extra ? xcd * (base + 1) + local : extra * (base + 1) + (xcd - extra) * base + local;
   const int per_group = GROUP_M * n_tiles;
   const int g = t / per_group;
   const int first_m = g * GROUP_M;

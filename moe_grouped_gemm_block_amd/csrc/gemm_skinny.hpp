@@ -23,13 +23,6 @@
 
 namespace dg {
 
-// s_waitcnt vmcnt(n) with expcnt / lgkmcnt at their maxima (n < 64).
-template <int N>
-__device__ __forceinline__ void wait_vmem_n() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
-}
-
 template <int MI, int NI, bool OUT_BF16>
 __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p) {
   constexpr int NW = 4;                         // waves, each a quarter of the K-blocks
