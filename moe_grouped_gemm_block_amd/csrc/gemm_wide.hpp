@@ -209,11 +209,21 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& p) {
     for (int st = 0; st < 4; ++st) af[st] = *reinterpret_cast<const v8h*>(a16 + (a16_base ^ (16 * st)));
     v4f part[NI];
     int4 xa;                                     // FP8 A granule between its read and its conversion
+    uint2 yb[NI];                                // raw FP8 B of one next-block operand, read a group ahead
+    // next block's B operand st of this lane: FP8 bytes 8 st .. 8 st + 7 of
+    // its 32-byte slice, i.e. half st & 1 of granule st >> 1
+    auto read_b8 = [&](int st) {
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        yb[ni] = *reinterpret_cast<const uint2*>(lb + ((st >> 1) ? b_off1 : b_off0) + 8 * (st & 1) + ni * 16 * KBLK);
+    };
+    // The body is a sequence of (row step mi, K sub-step st) groups separated
+    // by scheduling fences: each group holds its 4 MFMAs, the rescale FMAs of
+    // the previous row step (st = 0), the LDS read of the next row step's
+    // operand st (one full step of latency before its use) and its share of
+    // the A / B conversion work.  Inside a group the scheduler interleaves.
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-      if (mi == 1 || mi == 3) xa = read_a8(a8_next, mi >> 1);
-      if (mi == 2 || mi == 4) write_a16(a16_next, (mi - 2) >> 1, xa);
-      if (mi == MI - 1) wait_vmem_n<A_CH>();   // B(kb+1) landed (A(kb+2) may not have)
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
 #pragma unroll
@@ -231,50 +241,26 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& p) {
           // operand st of the next K-block's B, converted into the registers
           // the MFMAs above have just consumed (unconditionally: on the last
           // K-block this converts data that is never used, which keeps the
-          // old and new B values from both being live)
+          // old and new B values from both being live); its raw bytes were
+          // read one group earlier, the next operand's are read now
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni) {
-            const int h = st >> 1;
-            const int4 y = *reinterpret_cast<const int4*>(lb + (h ? b_off1 : b_off0) + ni * 16 * KBLK);
-            const uint32_t w0 = uint32_t((st & 1) ? y.z : y.x), w1 = uint32_t((st & 1) ? y.w : y.y);
             uint32_t hh[4];
-            fp8x4_to_f16(w0, hh[0], hh[1]);
-            fp8x4_to_f16(w1, hh[2], hh[3]);
+            fp8x4_to_f16(yb[ni].x, hh[0], hh[1]);
+            fp8x4_to_f16(yb[ni].y, hh[2], hh[3]);
             bh[ni][st] = __builtin_bit_cast(v8h, (uint4{hh[0], hh[1], hh[2], hh[3]}));
           }
+          if (st < 3) read_b8(st + 1);
         }
-      }
-      // Pin the order of this row step so that the scheduler does not hoist
-      // later steps' LDS reads (and their registers) above these MFMAs.
-      if (mi > 0) {
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // rescale of the previous step
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        if (mi == MI - 2 && st == 3) {
+          wait_vmem_n<A_CH>();                   // B(kb+1) landed (A(kb+2) may not have)
+          read_b8(0);
         }
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, NI, 0);
-      }
-      if (mi == 1 || mi == 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // A8 granule
-      if (mi + 1 < MI) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // next step's operand 0
-#pragma unroll
-        for (int st = 1; st < 4; ++st) {
-          if (mi == 2 || mi == 4) {                            // A conversion, 3 + 3 + 2
-            if (st < 3) __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-            else __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, NI, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        if (mi == 2 || mi == 4) __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // A16 stores
-      } else {
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          if (st > 0) __builtin_amdgcn_sched_group_barrier(0x008, NI, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, NI, 0);  // next block's raw B
-          __builtin_amdgcn_sched_group_barrier(0x002, 4 * NI, 0);  // its conversion
-        }
+        // A(kb+1): FP8 granule h read in step 1 + 2h, converted and stored in
+        // step 2 + 2h
+        if ((mi == 1 || mi == 3) && st == 1) xa = read_a8(a8_next, mi >> 1);
+        if ((mi == 2 || mi == 4) && st == 2) write_a16(a16_next, (mi - 2) >> 1, xa);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
