@@ -40,9 +40,12 @@ int check_common(const void* A, const float* sA, const void* B, const float* sB,
 
 // Tile shape of one launch.  Every wave owns a 64 x 128 sub-tile.  The
 // 128 x 512 tile runs 8 waves (two per SIMD, one workgroup per CU, 160 KB of
-// LDS); the 128 x 256 tile runs 4 waves and serves narrow problems.
+// LDS); the 128 x 256 tile runs 4 waves, serves narrow problems and finishes
+// the last partial round of a large problem (see launch()); the 128 x 128
+// tile (2 waves, 64 KB of LDS) is the alternative for that last round.
 // DG_FORCE_TILE=512 or 256 overrides the choice, 1512 selects the 1 x 8
-// wave arrangement (tuning aids).
+// wave arrangement; DG_TAIL_TILE=0 / 128 / 256 switches off or sets the
+// tile of the last partial round (tuning aids).
 constexpr int kCUs = 256;
 
 int forced_tile() {
@@ -53,9 +56,20 @@ int forced_tile() {
   return v;
 }
 
+int tail_tile() {
+  static const int v = [] {
+    const char* e = getenv("DG_TAIL_TILE");
+    return e ? atoi(e) : 256;
+  }();
+  return v;
+}
+
+// One launch over the 128-row tiles [m_tile0, m_tile0 + m_tiles).
 int launch_tiles(dg::GemmArgs a, int bn, int threads, void (*k_bf16)(dg::GemmArgs),
-                 void (*k_f32)(dg::GemmArgs), int out_dtype, hipStream_t stream) {
-  a.m_tiles = int((int64_t(a.M) + 127) / 128);
+                 void (*k_f32)(dg::GemmArgs), int out_dtype, hipStream_t stream, int m_tile0 = 0,
+                 int m_tiles = -1) {
+  a.m_tile0 = m_tile0;
+  a.m_tiles = m_tiles >= 0 ? m_tiles : int((int64_t(a.M) + 127) / 128);
   a.n_tiles = int((int64_t(a.N) + bn - 1) / bn);
   const int64_t blocks = int64_t(a.m_tiles) * a.n_tiles;
   if (blocks <= 0) return DG_OK;
@@ -97,6 +111,28 @@ int launch(const dg::GemmArgs& a, int out_dtype, hipStream_t stream) {
   if (forced_tile() == 1512)
     return launch_tiles(a, 512, 512, dg::dg_gemm_wide_128x512_bf16, dg::dg_gemm_wide_128x512_f32, out_dtype,
                         stream);
+  if (use512 && forced_tile() == 0 && tail_tile() != 0) {
+    // A 128 x 512 tile takes about as long whether 1 or all 256 CUs are busy,
+    // so a last round that is only partly filled costs almost a full round.
+    // The row tiles that fill whole rounds go in one launch; the remaining
+    // rows follow as narrower tiles, many more and each a fraction of the
+    // work, in a second launch on the same stream (no workspace: every output
+    // tile is still computed whole by one workgroup).
+    const int64_t nt = (int64_t(a.N) + 511) / 512;
+    const int64_t T = m_tiles * nt;
+    const int64_t main_m = (T / kCUs) * kCUs / nt;
+    if (T % kCUs != 0 && main_m > 0 && main_m < m_tiles) {
+      int st = launch_tiles(a, 512, 512, dg::dg_gemm_128x512_bf16, dg::dg_gemm_128x512_f32, out_dtype, stream,
+                            0, int(main_m));
+      if (st != DG_OK) return st;
+      const int rest = int(m_tiles - main_m);
+      if (tail_tile() == 128)
+        return launch_tiles(a, 128, 128, dg::dg_gemm_128x128_bf16, dg::dg_gemm_128x128_f32, out_dtype, stream,
+                            int(main_m), rest);
+      return launch_tiles(a, 256, 256, dg::dg_gemm_128x256_bf16, dg::dg_gemm_128x256_f32, out_dtype, stream,
+                          int(main_m), rest);
+    }
+  }
   if (use512)
     return launch_tiles(a, 512, 512, dg::dg_gemm_128x512_bf16, dg::dg_gemm_128x512_f32, out_dtype, stream);
   return launch_tiles(a, 256, 256, dg::dg_gemm_128x256_bf16, dg::dg_gemm_128x256_f32, out_dtype, stream);

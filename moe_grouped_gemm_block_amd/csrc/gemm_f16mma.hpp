@@ -144,7 +144,8 @@ struct GemmArgs {
   const int32_t* offs;    // [G+1] device, or nullptr for dense
   int G;
   int M, N, K;
-  int m_tiles, n_tiles;
+  int m_tiles, n_tiles;    // tiles of this launch
+  int m_tile0;            // first 128-row tile of this launch (a launch may cover a row range)
 };
 
 // Tile order: blockIdx -> (m-tile, n-tile).  Workgroups are dealt to the 8
@@ -187,7 +188,7 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int tm, tn;
   tile_of<8>(blockIdx.x, p.m_tiles, p.n_tiles, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = (p.m_tile0 + tm) * BM, n0 = tn * BN;
   const int M = p.M, N = p.N, K = p.K;
   const int Kb = K / KBLK;
   const int Nb = (N + KBLK - 1) / KBLK;
@@ -408,6 +409,8 @@ DG_GEMM_KERNEL(dg_gemm_128x512_bf16, 2, 4, true)
 DG_GEMM_KERNEL(dg_gemm_128x512_f32, 2, 4, false)
 DG_GEMM_KERNEL(dg_gemm_128x256_bf16, 2, 2, true)
 DG_GEMM_KERNEL(dg_gemm_128x256_f32, 2, 2, false)
+DG_GEMM_KERNEL(dg_gemm_128x128_bf16, 2, 1, true)
+DG_GEMM_KERNEL(dg_gemm_128x128_f32, 2, 1, false)
 #undef DG_GEMM_KERNEL
 
 }  // namespace dg

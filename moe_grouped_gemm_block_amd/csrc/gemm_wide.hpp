@@ -76,7 +76,7 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int tm, tn;
   tile_of<8>(blockIdx.x, p.m_tiles, p.n_tiles, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = (p.m_tile0 + tm) * BM, n0 = tn * BN;
   const int M = p.M, N = p.N, K = p.K;
   const int Kb = K / KBLK;
   const int Nb = (N + KBLK - 1) / KBLK;

@@ -234,3 +234,49 @@ def test_grouped_configs_sampled(i):
     for e in range(p.G):
         lo = off[e] + counts[e]
         assert np.all(Cg[lo:off[e + 1]] == 0)
+
+
+# ----------------------------------------------------------------- last-round split
+# 33 row tiles x 8 column tiles of 128 x 512 = 264 tiles: the first 32 row tiles
+# fill one round of 256 CUs, the 33rd runs as narrower tiles in a second
+# launch.  N = 4104 also leaves a partial last column tile in both launches.
+
+@pytest.mark.parametrize("N", [4096, 4104])
+def test_last_round_split_dense(N):
+    M, K = 33 * 128, 256
+    log(f"last-round split dense M={M} N={N} K={K}")
+    p = I.dense_problem(M, N, K, seed=N, out_dtype="bf16", block_log2_range=3.0)
+    Cg = as64(run(p))
+    rows = sample_rows(M, extra=list(range(32 * 128 - 2, 32 * 128 + 3)) + [M - 1], n=24, seed=N)
+    check(p, Cg, rows=rows, what=f"split dense N={N}")
+
+
+def grouped_fixed(counts, N, K, seed, out_dtype):
+    """Grouped problem with given per-expert row counts (each segment padded
+    to a multiple of 128 with zero rows), quantised by the shared generator."""
+    rng = np.random.default_rng(seed)
+    G = len(counts)
+    padded = [-(-c // 128) * 128 for c in counts]
+    offs = np.concatenate([[0], np.cumsum(padded)]).astype(np.int32)
+    A = np.zeros((int(offs[-1]), K), np.float32)
+    for e, c in enumerate(counts):
+        A[offs[e]:offs[e] + c] = rng.standard_normal((c, K), dtype=np.float32)
+    qA, sA = I.quantize(A)
+    qB = np.empty((G, N, K), np.uint8)
+    sB = np.empty((G, -(-N // 128), K // 128), np.float32)
+    for e in range(G):
+        qB[e], sB[e] = I.quantize(rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02))
+    return I.Problem(name="grouped_fixed", A=qA, sA=sA, B=qB, sB=sB, M=int(offs[-1]), N=N, K=K,
+                     out_dtype=out_dtype, seed=seed, group_offsets=offs, real_rows=int(sum(counts)))
+
+
+def test_last_round_split_grouped():
+    log("last-round split grouped")
+    N, K = 4096, 256
+    # segments of 1024, 2048 and 1152 rows (1100 padded): 33 row tiles
+    p = grouped_fixed([1024, 2048, 1100], N, K, seed=17, out_dtype="f32")
+    Cg = as64(run(p))
+    off = p.group_offsets
+    extra = [o for o in off[1:-1]] + [o - 1 for o in off[1:]] + list(range(4094, 4100))
+    rows = sample_rows(p.M, extra=extra, n=24, seed=17)
+    check(p, Cg, rows=rows, what="split grouped")
