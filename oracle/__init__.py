@@ -1,7 +1,9 @@
-"""CPU oracle for the FP8 block-scaled GEMM -- test infrastructure only.
+"""CPU oracle for the FP8 block-scaled GEMM and the activation quantisation
+that feeds it -- test infrastructure only.
 
 Used by tests/, the smoke check and the benchmark's CPU-baseline leg; never by
 the product path.
 """
 from .blockscaled import (BLOCK, decode, decode_table, e4m3_value,  # noqa: F401
                           gemm_blockscaled, grouped_gemm, tolerance)
+from .quantize import encode_nearest, quantize_blockscaled  # noqa: F401
