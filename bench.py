@@ -2,6 +2,7 @@
 """Benchmark of the FP8 block-scaled GEMM hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload I]
+    python bench.py --op quantize [--block-rows 128|1]
 
 A step is one GEMM call (dense or grouped) over one batch of seeded synthetic
 operands already resident in HBM.  W untimed warm-up steps are followed by
@@ -22,6 +23,9 @@ Workloads (seeded, synthetic; see inputs.make_config):
   3  skinny 64 x 12288 x 4096, outliers, BF16   (HBM-bound)
   4  MoE 8 experts, N = K = 4096, top-2 uniform
   5  MoE 64 experts, N = K = 2048, top-2 Zipf(1.1)
+
+--op quantize times the activation quantisation that produces A instead
+(4096 x 4096 BF16 in, E4M3 codes and FP32 block scales out; HBM-bound).
 """
 from __future__ import annotations
 
@@ -41,6 +45,7 @@ PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA (no sparsity)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 INFINITY_CACHE = 256 << 20
 HBM_BOUND = {3, 5}           # workloads whose roofline is HBM bandwidth
+QUANT_METRIC = "FP8 activation quantisation HBM GB/s (BF16 in, E4M3 + FP32 block scales out)"
 
 
 def gemm_tflops(M: int, N: int, K: int, seconds: float) -> float:
@@ -114,6 +119,92 @@ def cpu_baseline(p, target_s: float = 12.0):
                       f"{p.name}, float64 numpy/BLAS"}
 
 
+def cpu_baseline_quant(x, block_rows: int, target_s: float = 10.0):
+    """Time the quantisation oracle (as it stands) on rows of the same input."""
+    import numpy as np
+
+    import oracle
+    M, K = x.shape
+    step = block_rows                       # whole row blocks
+    t = time.perf_counter()
+    oracle.quantize_blockscaled(x[:step], block_rows)
+    dt = time.perf_counter() - t
+    n = int(min(M, max(step, step * round(target_s / max(dt, 1e-6)))))
+    n = max(step, n - n % step)
+    t = time.perf_counter()
+    oracle.quantize_blockscaled(x[:n], block_rows)
+    dt = time.perf_counter() - t
+    nbytes = n * K * (2 + 1) + 4 * (n // block_rows) * (K // 128)
+    return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"first {n} of {M} rows (all {K} columns) of the same input, numpy float64, "
+                      "one thread (per-block Python loop)"}
+
+
+def bench_quantize(args):
+    import numpy as np
+    import torch
+
+    from moe_grouped_gemm_block_amd import dg
+    dev = torch.device("cuda:0")
+    dg.lib()
+    M = K = 4096
+    R_blk = args.block_rows
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x *= np.repeat(np.repeat(np.exp2(rng.uniform(-4, 4, (M // 128, K // 128))).astype(np.float32),
+                             128, axis=0), 128, axis=1)
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    x_seen = xb.float().numpy()
+    step_bytes = M * K * 2 + M * K + 4 * (-(-M // R_blk)) * (K // 128)
+    R = args.rotate or max(1, -(-2 * INFINITY_CACHE // step_bytes))
+    copies = []
+    for _ in range(R):
+        X = xb.to(dev)
+        Q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        S = torch.empty((-(-M // R_blk), K // 128), dtype=torch.float32, device=dev)
+        copies.append((X, Q, S))
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step(i):
+        X, Q, S = copies[i % R]
+        st = dg.dg_quantize_fp8_blockscaled(X.data_ptr(), dg.DG_IN_BF16, Q.data_ptr(), S.data_ptr(),
+                                            M, K, R_blk, sh)
+        if st != dg.DG_OK:
+            raise dg.DGError(st, "bench step")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    n = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    t_start = time.perf_counter()
+    for i in range(n):
+        ev[i].record(stream)
+        step(args.warmup + i)
+    ev[n].record(stream)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_step = (t_end - t_start) * 1e3 / n
+    kern_ms = float(ev[0].elapsed_time(ev[n])) / n
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+    log(f"kernel ms (HIP events): mean {kern_ms:.4f}  p10 {np.percentile(per, 10):.4f}  "
+        f"p50 {np.percentile(per, 50):.4f}  p90 {np.percentile(per, 90):.4f}; wall ms/step {ms_step:.4f}")
+    name = f"quantize_{M}x{K}_bf16_{R_blk}x128"
+    achieved = step_bytes / (kern_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(name)}
+    cpu = None if args.no_cpu_baseline else cpu_baseline_quant(x_seen, R_blk)
+    line = {"metric": QUANT_METRIC, "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16->e4m3",
+            "data": "synthetic",
+            "config": {"workload": name, "M": M, "K": K, "block_rows": R_blk, "seed": 2, "operand_copies": R},
+            "roofline": roof, "cpu_baseline": cpu, "kernel_ms": round(kern_ms, 5)}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +213,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--rotate", type=int, default=0, help="operand copies (0 = enough to exceed the Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", choices=["gemm", "quantize"], default="gemm")
+    ap.add_argument("--block-rows", type=int, default=128, choices=[1, 128],
+                    help="--op quantize: rows per scale block")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times) and exit; "
                          "used to scale the HBM byte counters of the profiler")
@@ -152,6 +246,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copied {args.copy_calibration} MiB x 5 (reads {n} B, writes {n} B per copy)")
+        return
+    if args.op == "quantize":
+        bench_quantize(args)
         return
     dg.lib()
 

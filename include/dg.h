@@ -111,6 +111,42 @@ int dg_grouped_gemm_fp8(const void* A, const float* sA,
                         int num_groups, int64_t M_total, int64_t N, int64_t K,
                         int out_dtype, hipStream_t stream);
 
+typedef enum {
+  DG_IN_F32 = 0,    /* X is float32 */
+  DG_IN_BF16 = 1    /* X is bfloat16 */
+} dg_in_dtype;
+
+/*
+ * FP8 (E4M3FN) block quantisation of activations: the step that produces the
+ * A operand and its scales, re-run on every inference (block-wise scaling,
+ * FP8-for-MoE page, section 2.1, activations re-scaled at run time, section
+ * 4.3; amax-based dynamic scaling, the low-precision essay,
+ * hotelren.com/news/5702847, section 2.1).  Per block of block_rows rows x
+ * 128 columns:
+ *
+ *   amax = max |x|;   s = fp32(amax / 448), or 1 if the block is all zero;
+ *   Q    = the E4M3FN code nearest to x / s (quotient in double precision),
+ *          ties to the even code, magnitude capped at 448, sign bit of x.
+ *
+ *   X          : [M][K] row-major, in_dtype (DG_IN_F32 or DG_IN_BF16)
+ *   Q          : E4M3FN bytes [M][K] row-major (the layout A of the GEMMs takes)
+ *   S          : float32 [ceil(M / block_rows)][K/128] row-major
+ *   block_rows : 128 (the 128 x 128 blocks the GEMM entry points consume as
+ *                sA) or 1 (one scale per token and 128-column group, the
+ *                1 x 128 granularity of the FP8 kernel write-up, section 5.2)
+ *
+ * Shared conventions above apply (caller-owned device memory, asynchronous on
+ * `stream`, host-side argument checks).  X and Q must be 16-byte aligned, S
+ * 4-byte aligned.  DG_ERR_INVALID_ARG: unknown in_dtype or block_rows,
+ * negative or too large sizes, null or misaligned pointers for non-empty
+ * work.  DG_ERR_UNSUPPORTED: K not a multiple of 128 or above 2^22.  M == 0 or
+ * K == 0 is a no-op.  Non-finite inputs give unspecified codes (never a
+ * fault).
+ */
+int dg_quantize_fp8_blockscaled(const void* X, int in_dtype, void* Q, float* S,
+                                int64_t M, int64_t K, int block_rows,
+                                hipStream_t stream);
+
 /* Static, NUL-terminated description of a dg_status value. */
 const char* dg_status_string(int status);
 

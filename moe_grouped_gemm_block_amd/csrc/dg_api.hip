@@ -11,6 +11,7 @@
 #include "gemm_f16mma.hpp"
 #include "gemm_skinny.hpp"
 #include "gemm_wide.hpp"
+#include "quant.hpp"
 
 namespace {
 
@@ -181,6 +182,28 @@ int dg_grouped_gemm_fp8(const void* A, const float* sA, const void* B, const flo
   a.N = int(N);
   a.K = int(K);
   return launch(a, out_dtype, stream);
+}
+
+int dg_quantize_fp8_blockscaled(const void* X, int in_dtype, void* Q, float* S, int64_t M, int64_t K,
+                                int block_rows, hipStream_t stream) {
+  if (in_dtype != DG_IN_F32 && in_dtype != DG_IN_BF16) return DG_ERR_INVALID_ARG;
+  if (block_rows != 1 && block_rows != 128) return DG_ERR_INVALID_ARG;
+  if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim) return DG_ERR_INVALID_ARG;
+  if (M == 0 || K == 0) return DG_OK;
+  if (X == nullptr || Q == nullptr || S == nullptr) return DG_ERR_INVALID_ARG;
+  if (!aligned(X, 16) || !aligned(Q, 16) || !aligned(S, 4)) return DG_ERR_INVALID_ARG;
+  if (K % dg::KBLK != 0 || K > kMaxK) return DG_ERR_UNSUPPORTED;
+  dg::QuantArgs a{X, static_cast<uint8_t*>(Q), S, int(M), int(K)};
+  const int64_t Kb = K / dg::KBLK;
+  const int64_t blocks = block_rows == 128 ? ((M + 127) / 128) * Kb : (M * Kb + 3) / 4;
+  if (blocks > INT32_MAX) return DG_ERR_UNSUPPORTED;
+  const bool bf16 = in_dtype == DG_IN_BF16;
+  const void* fn = block_rows == 128
+      ? (bf16 ? reinterpret_cast<const void*>(dg::dg_quant_128x128_bf16) : reinterpret_cast<const void*>(dg::dg_quant_128x128_f32))
+      : (bf16 ? reinterpret_cast<const void*>(dg::dg_quant_1x128_bf16) : reinterpret_cast<const void*>(dg::dg_quant_1x128_f32));
+  void* kargs[] = {&a};
+  hipError_t err = hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(256), kargs, 0, stream);
+  return err == hipSuccess ? DG_OK : DG_ERR_LAUNCH;
 }
 
 const char* dg_status_string(int status) {

@@ -19,12 +19,15 @@ LIB_PATH = os.environ.get("DG_LIBRARY", os.path.join(_PKG, "libdg.so"))
 
 DG_OUT_F32 = 0
 DG_OUT_BF16 = 1
+DG_IN_F32 = 0
+DG_IN_BF16 = 1
 DG_OK = 0
 DG_ERR_INVALID_ARG = -1
 DG_ERR_UNSUPPORTED = -2
 DG_ERR_LAUNCH = -3
 
-EXPORTED = ("dg_gemm_fp8_blockscaled", "dg_grouped_gemm_fp8", "dg_status_string")
+EXPORTED = ("dg_gemm_fp8_blockscaled", "dg_grouped_gemm_fp8", "dg_quantize_fp8_blockscaled",
+            "dg_status_string")
 
 _lib = None
 
@@ -43,6 +46,8 @@ def lib() -> ctypes.CDLL:
         L.dg_gemm_fp8_blockscaled.restype = ci
         L.dg_grouped_gemm_fp8.argtypes = [vp, vp, vp, vp, vp, vp, ci, i64, i64, i64, ci, vp]
         L.dg_grouped_gemm_fp8.restype = ci
+        L.dg_quantize_fp8_blockscaled.argtypes = [vp, ci, vp, vp, i64, i64, ci, vp]
+        L.dg_quantize_fp8_blockscaled.restype = ci
         L.dg_status_string.argtypes = [ci]
         L.dg_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -59,6 +64,10 @@ def dg_grouped_gemm_fp8(A, sA, B, sB, C, group_offsets, num_groups, M_total, N, 
                         out_dtype, stream) -> int:
     return lib().dg_grouped_gemm_fp8(A, sA, B, sB, C, group_offsets, num_groups, M_total,
                                      N, K, out_dtype, stream)
+
+
+def dg_quantize_fp8_blockscaled(X, in_dtype, Q, S, M, K, block_rows, stream) -> int:
+    return lib().dg_quantize_fp8_blockscaled(X, in_dtype, Q, S, M, K, block_rows, stream)
 
 
 def dg_status_string(status: int) -> str:
@@ -159,3 +168,31 @@ def grouped_gemm_fp8(A, sA, B, sB, group_offsets, out_dtype="bf16", C=None, stre
     if st != DG_OK:
         raise DGError(st, "dg_grouped_gemm_fp8")
     return C
+
+
+def quantize_fp8_blockscaled(X, block_rows=128, Q=None, S=None, stream=None):
+    """E4M3 codes and FP32 block scales of X[M][K] (float32 or bfloat16), one
+    scale per block_rows x 128 block (block_rows = 128 or 1)."""
+    torch = _torch()
+    if X.dtype == torch.float32:
+        code = DG_IN_F32
+    elif X.dtype == torch.bfloat16:
+        code = DG_IN_BF16
+    else:
+        raise TypeError(f"X must be float32 or bfloat16, got {X.dtype}")
+    if not X.is_cuda or not X.is_contiguous() or X.dim() != 2:
+        raise ValueError("X must be a contiguous 2-D device tensor")
+    M, K = X.shape
+    if Q is None:
+        Q = torch.empty((M, K), dtype=torch.uint8, device=X.device)
+    if S is None:
+        S = torch.empty((-(-M // block_rows), K // 128), dtype=torch.float32, device=X.device)
+    _check_fp8(Q, "Q")
+    _check_f32(S, "S", (-(-M // block_rows), K // 128))
+    if tuple(Q.shape) != (M, K):
+        raise ValueError("Q must have the shape of X")
+    st = dg_quantize_fp8_blockscaled(X.data_ptr(), code, Q.data_ptr(), S.data_ptr(), M, K, block_rows,
+                                     _stream(stream))
+    if st != DG_OK:
+        raise DGError(st, "dg_quantize_fp8_blockscaled")
+    return Q, S

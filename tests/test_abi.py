@@ -40,7 +40,7 @@ def L():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() >= {"dg_gemm_fp8_blockscaled", "dg_grouped_gemm_fp8",
-                                    "dg_status_string"}
+                                    "dg_quantize_fp8_blockscaled", "dg_status_string"}
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -90,6 +90,22 @@ def test_dense_validation(L, kw, want):
 ])
 def test_grouped_validation(L, kw, want):
     assert grouped(**kw) == want
+
+
+def quant(X=P, dt=1, Q=P, S=P, M=256, K=256, R=128):
+    return dg.dg_quantize_fp8_blockscaled(X, dt, Q, S, M, K, R, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dt=2), INVALID), (dict(dt=-1), INVALID), (dict(R=64), INVALID), (dict(R=0), INVALID),
+    (dict(X=None), INVALID), (dict(Q=None), INVALID), (dict(S=None), INVALID),
+    (dict(X=P + 8), INVALID), (dict(Q=P + 4), INVALID), (dict(S=P + 2), INVALID),
+    (dict(M=-1), INVALID), (dict(K=-128), INVALID), (dict(M=1 << 31), INVALID),
+    (dict(K=200), UNSUP), (dict(K=1 << 23), UNSUP), (dict(K=64, R=1), UNSUP),
+    (dict(M=0), OK), (dict(K=0), OK), (dict(M=0, X=None, Q=None, S=None), OK),
+])
+def test_quantize_validation(L, kw, want):
+    assert quant(**kw) == want
 
 
 def test_product_path_does_not_touch_the_oracle():
