@@ -195,7 +195,7 @@ int dg_quantize_fp8_blockscaled(const void* X, int in_dtype, void* Q, float* S, 
   if (K % dg::KBLK != 0 || K > kMaxK) return DG_ERR_UNSUPPORTED;
   dg::QuantArgs a{X, static_cast<uint8_t*>(Q), S, int(M), int(K)};
   const int64_t Kb = K / dg::KBLK;
-  const int64_t blocks = block_rows == 128 ? ((M + 127) / 128) * Kb : (M * Kb + 3) / 4;
+  const int64_t blocks = block_rows == 128 ? ((M + 127) / 128) * Kb : (M * Kb + 15) / 16;
   if (blocks > INT32_MAX) return DG_ERR_UNSUPPORTED;
   const bool bf16 = in_dtype == DG_IN_BF16;
   const void* fn = block_rows == 128

@@ -13,18 +13,23 @@
 // (demingchina.com/news/60142), section 5.2; E4M3 range: same write-up,
 // section 3.1.
 //
-// Exactness.  The quotient is the correctly rounded double x / s.  An E4M3
-// midpoint m has at most 5 significant bits, so m s is exact in 29 bits.  If
-// x = m s the double quotient is exactly m (a tie, resolved to even); if not,
-// x and m s are distinct multiples of a unit at most 2^-29 |m s|, so
-// |x / s - m| is far above the double's 2^-53 relative rounding error and
-// rounding the double gives the same code as rounding the exact quotient.
+// Exactness without a per-element division.  Per block the scale is brought
+// to s_n = s 2^-e in [0.5, 1) by its binary exponent e (exact, subnormal s
+// included) and each |x| to a = |x| 2^-e (exact: a <= |x| / s * s_n < 448 can
+// not overflow, and an a that underflows is far below the first E4M3
+// midpoint).  An approximate quotient y = a * fp32(1 / s_n), within a few
+// ulp of a / s_n, only picks the two E4M3 grid values lo < hi around it; the
+// nearest grid value of the exact quotient is always one of them, because
+// grid steps are at least 2^-3 of the value.  The choice is then exact: the
+// midpoint m = (lo + hi) / 2 has at most 5 significant bits, so
+// fma(m, s_n, -a) has the sign of m s_n - a, i.e. of m - |x| / s, and is zero
+// only at an exact tie, which goes to the even grid index.  Binade edges need
+// no special case: a grid index of 16 carries into the exponent field.
 // The scale fp32(double(amax) / 448) equals the IEEE FP32 quotient (double
 // rounding through 53 bits is innocuous for one division of 24-bit numbers).
 //
 // Memory-bound: each element is read once (2 or 4 bytes) and written once
-// (1 byte); the per-element double division is a few percent of the issue
-// slots at this traffic.
+// (1 byte); about 20 FP32 / integer instructions per element.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,21 +44,40 @@ struct QuantArgs {
   int M, K;
 };
 
-// double -> E4M3FN code: nearest value, ties to even, capped at 448.
-__device__ __forceinline__ uint32_t e4m3_rne(double q) {
-  const uint32_t sign = uint32_t(uint64_t(__double_as_longlong(q)) >> 63) << 7;   // 0 or 0x80
-  const double a = __builtin_fabs(q);
-  if (!(a < 448.0)) return sign | 0x7Eu;                  // saturate (also NaN: unspecified input)
-  if (a < 0.015625) {                                     // below 2^-6: steps of 2^-9
-    return sign | uint32_t(__builtin_rint(a * 512.0));    // 0 .. 8 (8 = 2^-6, code 0x08)
-  }
-  // a in [2^E, 2^(E+1)), -6 <= E <= 8: 8 steps of 2^(E-3) per binade
-  const int E = int((__double_as_longlong(a) >> 52) & 0x7FF) - 1023;
-  const double to_steps = __longlong_as_double((long long)(1023 + 3 - E) << 52);   // 2^(3-E), exact
-  uint32_t m = uint32_t(__builtin_rint(a * to_steps));    // 8 .. 16 (16: carried into the next binade)
-  uint32_t e = uint32_t(E + 7);
-  if (m == 16) { m = 8; e += 1; }                         // a < 448 keeps this below 448
-  return sign | (e << 3) | (m - 8);
+// Per-block constants of the exact encoder (see "Exactness" above).
+struct ScaleNorm {
+  int e;        // s = s_n 2^e
+  float s_n;    // in [0.5, 1)
+  float inv_n;  // fp32(1 / s_n), in (1, 2]
+};
+
+__device__ __forceinline__ ScaleNorm scale_norm(float s) {
+  ScaleNorm n;
+  n.e = __builtin_amdgcn_frexp_expf(s);
+  n.s_n = __builtin_amdgcn_frexp_mantf(s);
+  n.inv_n = 1.0f / n.s_n;
+  return n;
+}
+
+// E4M3FN code of x / s: nearest value, ties to even, capped at 448, sign of x.
+__device__ __forceinline__ uint32_t e4m3_code(float x, const ScaleNorm& n) {
+  const uint32_t sign = (__float_as_uint(x) >> 31) << 7;
+  const float a = __builtin_ldexpf(__builtin_fabsf(x), -n.e);
+  const float y = a * n.inv_n;                            // ~ |x| / s
+  // grid around y: below 2^-6 steps of 2^-9 (codes 0 .. 8); in [2^E, 2^(E+1))
+  // steps of 2^(E-3) (codes (E+7) << 3 | 0 .. 7); step index k of lo
+  const int E = max(int((__float_as_uint(y) >> 23) & 0xFF) - 127, -6);
+  const float step = __uint_as_float(uint32_t(E - 3 + 127) << 23);        // 2^(E-3)
+  const float k = __builtin_floorf(__builtin_ldexpf(y, 3 - E));          // exact scaling
+  const float mid = (k + 0.5f) * step;                                    // exact (5 bits)
+  const float r = __builtin_fmaf(mid, n.s_n, -a);                         // sign of mid - |x|/s
+  const uint32_t ki = uint32_t(k);
+  const uint32_t kk = ki + uint32_t(r < 0.f || (r == 0.f && (ki & 1u)));  // nearest, ties to even
+  // code ((E + 7) << 3) + kk - 8: also right below 2^-6 (E clamped to -6,
+  // kk = 0 .. 8 are the subnormal codes and 2^-6), and kk = 16 carries into
+  // the next binade
+  const uint32_t code = (uint32_t(E + 7) << 3) + kk - 8u;
+  return sign | min(code, 0x7Eu);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -114,7 +138,7 @@ __device__ __forceinline__ void quant128_body(const QuantArgs& p) {
   __syncthreads();
   amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const float s = scale_of(amax);
-  const double sd = double(s);
+  const ScaleNorm sn = scale_norm(s);
   if (valid) {
     uint4* dst = reinterpret_cast<uint4*>(p.Q + e0);
 #pragma unroll
@@ -124,7 +148,7 @@ __device__ __forceinline__ void quant128_body(const QuantArgs& p) {
       for (int j = 0; j < 4; ++j) {
         uint32_t packed = 0;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) packed |= e4m3_rne(double(v[16 * i + 4 * j + b]) / sd) << (8 * b);
+        for (int b = 0; b < 4; ++b) packed |= e4m3_code(v[16 * i + 4 * j + b], sn) << (8 * b);
         w[j] = packed;
       }
       dst[i] = uint4{w[0], w[1], w[2], w[3]};
@@ -133,31 +157,58 @@ __device__ __forceinline__ void quant128_body(const QuantArgs& p) {
   if (t == 0) p.S[size_t(rb) * Kb + kb] = s;
 }
 
-// 1 x 128 blocks: one wave per (row, 128-column group), block index
-// row * Kb + kb = 4 * workgroup + wave; lane L holds columns 2L, 2L + 1.
+// 1 x 128 blocks.  Block b = row * Kb + kb covers elements [128 b, 128 b + 128)
+// of the row-major matrix, so consecutive blocks are contiguous: a wave
+// takes 4 of them (16 lanes each, 8 elements per lane: one 16-byte load of
+// BF16, two of FP32), a workgroup 16.  amax is reduced within the 16 lanes.
+__device__ __forceinline__ float group16_max(float v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
 template <bool IN_BF16>
 __device__ __forceinline__ void quant1_body(const QuantArgs& p) {
-  const int Kb = p.K / 128;
+  const long long nblk = (long long)p.M * (p.K / 128);
   const int lane = threadIdx.x & 63;
-  const long long blk = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (blk >= (long long)p.M * Kb) return;       // whole wave; no barrier in this kernel
-  const int m = int(blk / Kb), kb = int(blk % Kb);
-  const size_t e0 = size_t(m) * p.K + size_t(kb) * 128 + 2 * lane;
-  float v0, v1;
-  if constexpr (IN_BF16) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.X) + e0);
-    v0 = bf16_to_f32(w & 0xFFFFu);
-    v1 = bf16_to_f32(w >> 16);
+  const long long b = (long long)blockIdx.x * 16 + (threadIdx.x >> 6) * 4 + (lane >> 4);
+  const bool valid = b < nblk;
+  const size_t e0 = size_t(b) * 128 + size_t(lane & 15) * 8;   // first element of this lane
+  float v[8];
+  if (valid) {
+    if constexpr (IN_BF16) {
+      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.X) + e0);
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = bf16_to_f32(u[j] & 0xFFFFu);
+        v[2 * j + 1] = bf16_to_f32(u[j] >> 16);
+      }
+    } else {
+      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(p.X) + e0);
+      const float4 w0 = src[0], w1 = src[1];
+      v[0] = w0.x; v[1] = w0.y; v[2] = w0.z; v[3] = w0.w;
+      v[4] = w1.x; v[5] = w1.y; v[6] = w1.z; v[7] = w1.w;
+    }
   } else {
-    const float2 w = *reinterpret_cast<const float2*>(static_cast<const float*>(p.X) + e0);
-    v0 = w.x; v1 = w.y;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.f;                    // joins the reduction, stores nothing
   }
-  const float amax = wave_max(fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1)));
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, __builtin_fabsf(v[i]));
+  amax = group16_max(amax);
   const float s = scale_of(amax);
-  const double sd = double(s);
-  const uint32_t c = e4m3_rne(double(v0) / sd) | (e4m3_rne(double(v1) / sd) << 8);
-  *reinterpret_cast<uint16_t*>(p.Q + e0) = uint16_t(c);
-  if (lane == 0) p.S[size_t(m) * Kb + kb] = s;
+  const ScaleNorm sn = scale_norm(s);
+  if (valid) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= e4m3_code(v[i], sn) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= e4m3_code(v[4 + i], sn) << (8 * i);
+    *reinterpret_cast<uint2*>(p.Q + e0) = uint2{lo, hi};
+    if ((lane & 15) == 0) p.S[b] = s;
+  }
 }
 
 #define DG_QUANT_KERNEL(NAME, BODY, BF16) \
