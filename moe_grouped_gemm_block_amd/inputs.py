@@ -45,6 +45,8 @@ import numpy as np
 
 BLOCK = 128
 E4M3_MAX = 448.0
+E5M2_MAX = 57344.0
+FMT_MAX = {"e4m3": E4M3_MAX, "e5m2": E5M2_MAX}
 
 
 # ---------------------------------------------------------------------------
@@ -79,8 +81,32 @@ def encode_e4m3(v: np.ndarray) -> np.ndarray:
     return code.astype(np.uint8)
 
 
-def block_scales(x: np.ndarray) -> np.ndarray:
-    """Per-128x128-block scale fp32(amax/448) of a float32 [R][K] matrix.
+def encode_e5m2(v: np.ndarray) -> np.ndarray:
+    """float64 values -> uint8 E5M2 codes (RNE, saturate at +-57344).
+
+    Same binade snapping as encode_e4m3 with 2 mantissa bits and exponent
+    bias 15: quantum 2^(e-2) in the binade [2^e, 2^(e+1)), e >= -14, and
+    2^-16 below 2^-14.  An E5M2 code is the high byte of the IEEE half with
+    the same value, which gives the bits directly.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    neg = np.signbit(v)
+    a = np.minimum(np.abs(v), E5M2_MAX)
+    _, ex = np.frexp(a)
+    e = np.maximum(ex - 1, -14)
+    quantum = np.ldexp(1.0, e - 2)
+    r = np.minimum(np.rint(a / quantum) * quantum, E5M2_MAX)    # exact half value with 2 mantissa bits
+    code = (r.astype(np.float16).view(np.uint16) >> 8).astype(np.int64)
+    code = code | (neg.astype(np.int64) << 7)
+    return code.astype(np.uint8)
+
+
+ENCODERS = {"e4m3": encode_e4m3, "e5m2": encode_e5m2}
+
+
+def block_scales(x: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
+    """Per-128x128-block scale fp32(amax/fmax) of a float32 [R][K] matrix
+    (fmax = 448 for E4M3, 57344 for E5M2).
 
     Returns float32 [ceil(R/128)][K/128]; all-zero blocks get 1.0.  The last
     row block may be partial (R not a multiple of 128).
@@ -93,23 +119,24 @@ def block_scales(x: np.ndarray) -> np.ndarray:
     if pad:
         xa = np.concatenate([xa, np.zeros((pad, K), np.float32)], axis=0)
     amax = xa.reshape(Rb, BLOCK, Kb, BLOCK).max(axis=(1, 3)).astype(np.float32)
-    s = amax / np.float32(E4M3_MAX)           # fp32 division, RNE
+    s = amax / np.float32(FMT_MAX[fmt])       # fp32 division, RNE
     s = np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
     return s
 
 
-def quantize(x: np.ndarray, row_chunk: int = 1024) -> tuple[np.ndarray, np.ndarray]:
+def quantize(x: np.ndarray, row_chunk: int = 1024, fmt: str = "e4m3") -> tuple[np.ndarray, np.ndarray]:
     """Quantise float32 [R][K] -> (codes uint8 [R][K], scales fp32 [Rb][Kb])."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     R, K = x.shape
-    s = block_scales(x)
+    s = block_scales(x, fmt)
+    enc = ENCODERS[fmt]
     q = np.empty((R, K), np.uint8)
     s64 = s.astype(np.float64)
     for r0 in range(0, R, row_chunk):           # bounded temporaries
         r1 = min(R, r0 + row_chunk)
         rows = np.arange(r0, r1) // BLOCK
         sexp = np.repeat(s64[rows], BLOCK, axis=1)          # [rows][K]
-        q[r0:r1] = encode_e4m3(x[r0:r1].astype(np.float64) / sexp)
+        q[r0:r1] = enc(x[r0:r1].astype(np.float64) / sexp)
     return q, s
 
 
@@ -137,6 +164,8 @@ class Problem:
     seed: int
     group_offsets: np.ndarray | None = None
     real_rows: int | None = None        # rows that carry tokens (grouped)
+    a_fmt: str = "e4m3"                 # code format of A / B: "e4m3" or "e5m2"
+    b_fmt: str = "e4m3"
 
     @property
     def grouped(self) -> bool:
@@ -169,9 +198,11 @@ def streams(seed: int) -> list[np.random.Generator]:
 def dense_problem(M: int, N: int, K: int, seed: int, out_dtype: str = "bf16",
                   a_std: float = 1.0, b_std: float = 1.0,
                   block_log2_range: float = 0.0, outlier_frac: float = 0.0,
-                  outlier_mult: float = 50.0, name: str = "dense") -> Problem:
+                  outlier_mult: float = 50.0, name: str = "dense",
+                  a_fmt: str = "e4m3", b_fmt: str = "e4m3") -> Problem:
     """Gaussian A [M][K] and B [N][K] with optional per-block multipliers and
-    per-element outliers, quantised to E4M3 with 128x128 block scales."""
+    per-element outliers, quantised to E4M3 (or E5M2) with 128x128 block
+    scales."""
     r_act, r_w, r_mod, _ = streams(seed)
     A = r_act.standard_normal((M, K), dtype=np.float32) * np.float32(a_std)
     B = r_w.standard_normal((N, K), dtype=np.float32) * np.float32(b_std)
@@ -186,10 +217,10 @@ def dense_problem(M: int, N: int, K: int, seed: int, out_dtype: str = "bf16",
     if outlier_frac:
         hit = r_mod.random((M, K)) < outlier_frac
         A[hit] *= np.float32(outlier_mult)
-    qA, sA = quantize(A)
-    qB, sB = quantize(B)
+    qA, sA = quantize(A, fmt=a_fmt)
+    qB, sB = quantize(B, fmt=b_fmt)
     return Problem(name=name, A=qA, sA=sA, B=qB, sB=sB, M=M, N=N, K=K,
-                   out_dtype=out_dtype, seed=seed)
+                   out_dtype=out_dtype, seed=seed, a_fmt=a_fmt, b_fmt=b_fmt)
 
 
 def route_top2(rng: np.random.Generator, T: int, weights: np.ndarray) -> np.ndarray:

@@ -65,27 +65,58 @@ def e4m3_value(code: int) -> float:
     return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
 
 
-def decode_table() -> np.ndarray:
-    """float64 [256]: value of every E4M3FN code."""
-    return np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+def e5m2_value(code: int) -> float:
+    """Value of one E5M2 byte, from its bit fields (the FP8 kernel write-up's
+    section 3.1 table: 1 sign, 5 exponent, 2 mantissa bits).
+
+    sign = bit 7, exponent field e = bits 6..2 (bias 15), mantissa m = bits 1..0.
+    e == 0: subnormal, m * 2^-16 (= m/4 * 2^-14).  e == 31: infinity (m == 0)
+    or NaN.  Otherwise (1 + m/4) * 2^(e - 15); the largest finite value is
+    1.75 * 2^15 = 57344.
+    """
+    sign = -1.0 if (code >> 7) & 1 else 1.0
+    e = (code >> 2) & 0x1F
+    m = code & 0x3
+    if e == 0x1F:
+        return sign * float("inf") if m == 0 else float("nan")
+    if e == 0:
+        return sign * m * 2.0 ** -16
+    return sign * (1.0 + m / 4.0) * 2.0 ** (e - 15)
 
 
-_LUT = decode_table()
+FORMATS = {"e4m3": e4m3_value, "e5m2": e5m2_value}
 
 
-def decode(codes: np.ndarray) -> np.ndarray:
+def decode_table(fmt: str = "e4m3") -> np.ndarray:
+    """float64 [256]: value of every code of the format ("e4m3" = OCP E4M3FN,
+    "e5m2")."""
+    return np.array([FORMATS[fmt](c) for c in range(256)], dtype=np.float64)
+
+
+_LUTS = {f: decode_table(f) for f in FORMATS}
+_LUT = _LUTS["e4m3"]
+
+
+def decode(codes: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
     """uint8 codes -> float64 values by table lookup."""
-    return _LUT[np.asarray(codes, dtype=np.uint8)]
+    return _LUTS[fmt][np.asarray(codes, dtype=np.uint8)]
 
 
 def gemm_blockscaled(A: np.ndarray, sA: np.ndarray, B: np.ndarray, sB: np.ndarray,
                      rows: np.ndarray | None = None,
-                     cols: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
+                     cols: np.ndarray | None = None,
+                     a_fmt: str = "e4m3", b_fmt: str = "e4m3") -> tuple[np.ndarray, np.ndarray]:
     """Dense block-scaled GEMM.
 
     A: uint8 [M][K] (row-major), sA: fp32 [ceil(M/128)][K/128]
     B: uint8 [N][K] (B column-major), sB: fp32 [ceil(N/128)][K/128]
     rows / cols: optional index subsets of the output to evaluate.
+    a_fmt / b_fmt: "e4m3" (default) or "e5m2" codes.
+
+    With an E5M2 operand a block partial can need more than 53 bits (E5M2
+    values span 2^-16 .. 57344), so it is then exact only up to BLAS's
+    summation error, at most 128 * 2^-53 of the block's sum |a b| -- far
+    inside the comparison tolerance.
 
     Returns (C, mass), both float64 [len(rows)][len(cols)], where
     mass[i, j] = sum_k |dec(A[i,k]) * dec(B[j,k])| * sA * sB (the magnitude the
@@ -98,15 +129,15 @@ def gemm_blockscaled(A: np.ndarray, sA: np.ndarray, B: np.ndarray, sB: np.ndarra
     Kb = K // BLOCK
     rows = np.arange(M) if rows is None else np.asarray(rows)
     cols = np.arange(N) if cols is None else np.asarray(cols)
-    A64 = decode(A[rows])                                     # [m][K]
-    B64 = decode(B[cols])                                     # [n][K]
+    A64 = decode(A[rows], a_fmt)                              # [m][K]
+    B64 = decode(B[cols], b_fmt)                              # [n][K]
     C = np.zeros((len(rows), len(cols)), np.float64)
     mass = np.zeros_like(C)
     for kb in range(Kb):
         ks = slice(kb * BLOCK, (kb + 1) * BLOCK)
         a = A64[:, ks]
         b = B64[:, ks]
-        partial = a @ b.T                                      # exact
+        partial = a @ b.T                                      # exact for E4M3 x E4M3
         absum = np.abs(a) @ np.abs(b).T                        # exact
         scale = (sA[rows // BLOCK, kb].astype(np.float64)[:, None]
                  * sB[cols // BLOCK, kb].astype(np.float64)[None, :])
@@ -118,7 +149,8 @@ def gemm_blockscaled(A: np.ndarray, sA: np.ndarray, B: np.ndarray, sB: np.ndarra
 def grouped_gemm(A: np.ndarray, sA: np.ndarray, B: np.ndarray, sB: np.ndarray,
                  group_offsets: np.ndarray,
                  rows: np.ndarray | None = None,
-                 cols: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
+                 cols: np.ndarray | None = None,
+                 a_fmt: str = "e4m3", b_fmt: str = "e4m3") -> tuple[np.ndarray, np.ndarray]:
     """MoE grouped block-scaled GEMM over contiguous expert segments.
 
     A: uint8 [M_total][K]; sA: fp32 [M_total/128][K/128]
@@ -146,7 +178,8 @@ def grouped_gemm(A: np.ndarray, sA: np.ndarray, B: np.ndarray, sB: np.ndarray,
         if lo % BLOCK:
             raise ValueError("segment starts must be multiples of 128")
         sA_e = sA[lo // BLOCK:(hi + BLOCK - 1) // BLOCK]
-        Ce, me = gemm_blockscaled(A[lo:hi], sA_e, B[e], sB[e], rows=local, cols=cols)
+        Ce, me = gemm_blockscaled(A[lo:hi], sA_e, B[e], sB[e], rows=local, cols=cols,
+                                  a_fmt=a_fmt, b_fmt=b_fmt)
         C[sel] = Ce
         mass[sel] = me
     return C, mass

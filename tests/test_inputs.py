@@ -128,3 +128,26 @@ def test_grouped_layout_small():
     for e in range(5):
         pad = p.A[off[e] + counts[e]:off[e + 1]]
         assert not pad.any()
+
+
+def test_e5m2_encoder_matches_library_cast():
+    """The generator's E5M2 encoder (binade snapping) against torch's RNE cast,
+    inside the finite range."""
+    import torch
+    rng = np.random.default_rng(7)
+    v = np.concatenate([rng.standard_normal(20000) * 3000, rng.uniform(-57344, 57344, 20000),
+                        rng.standard_normal(5000) * 1e-4]).astype(np.float32).astype(np.float64)
+    lib = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(I.encode_e5m2(v), lib)
+    assert I.encode_e5m2(np.array([1e9]))[0] == 0x7B and I.encode_e5m2(np.array([-1e9]))[0] == 0xFB
+
+
+def test_e5m2_problem_blocks_reach_the_format_max():
+    p = I.dense_problem(130, 136, 256, seed=1, a_fmt="e5m2", b_fmt="e5m2")
+    tab = (np.arange(256, dtype=np.uint16) << 8).view(np.float16).astype(np.float64)
+    for X, R in ((p.A, 130), (p.B, 136)):
+        for rb in range(-(-R // 128)):
+            for kb in range(2):
+                blk = X[rb * 128:(rb + 1) * 128, kb * 128:(kb + 1) * 128]
+                assert np.abs(tab[blk]).max() == 57344.0
+    assert p.a_fmt == "e5m2" and p.b_fmt == "e5m2"

@@ -262,7 +262,7 @@ def test_pins_catch_planted_decode_slips(monkeypatch, slip):
     else:
         sub = ((np.arange(256) >> 3) & 0xF) == 0
         tab[sub] = 0.0
-    monkeypatch.setattr(OB, "_LUT", tab)
+    monkeypatch.setitem(OB._LUTS, "e4m3", tab)
     with pytest.raises(AssertionError):
         test_brute_force_exact(8, 7, 256, 1)
 
