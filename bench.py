@@ -101,7 +101,7 @@ def cpu_baseline(p, target_s: float = 12.0):
         if p.grouped:
             oracle.grouped_gemm(p.A, p.sA, p.B, p.sB, p.group_offsets, rows=rows)
         else:
-            oracle.gemm_blockscaled(p.A, p.sA, p.B, p.sB, rows=rows)
+            oracle.gemm_blockscaled(p.A, p.sA, p.B, p.sB, rows=rows, a_fmt=p.a_fmt, b_fmt=p.b_fmt)
         return time.perf_counter() - t
 
     calib = np.sort(rng.choice(M, size=min(M, 64), replace=False))
@@ -214,6 +214,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="operand copies (0 = enough to exceed the Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--op", choices=["gemm", "quantize"], default="gemm")
+    ap.add_argument("--fmt", choices=["e4m3", "e5m2"], default="e4m3",
+                    help="operand FP8 format of the dense workloads 1-3 (both operands)")
     ap.add_argument("--block-rows", type=int, default=128, choices=[1, 128],
                     help="--op quantize: rows per scale block")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -253,7 +255,7 @@ def main():
     dg.lib()
 
     t0 = time.perf_counter()
-    p = I.make_config(args.workload)
+    p = I.make_config(args.workload, fmt=args.fmt)
     log(f"generated {p.name} in {time.perf_counter() - t0:.1f}s: M={p.M} N={p.N} K={p.K} "
         f"G={p.G} real_rows={p.real_rows}")
 
@@ -280,10 +282,14 @@ def main():
             st = dg.dg_grouped_gemm_fp8(d["A"].data_ptr(), d["sA"].data_ptr(), d["B"].data_ptr(),
                                         d["sB"].data_ptr(), d["C"].data_ptr(), d["offs"].data_ptr(),
                                         p.G, p.M, p.N, p.K, code, sh)
-        else:
+        elif p.a_fmt == "e4m3" and p.b_fmt == "e4m3":
             st = dg.dg_gemm_fp8_blockscaled(d["A"].data_ptr(), d["sA"].data_ptr(), d["B"].data_ptr(),
                                             d["sB"].data_ptr(), d["C"].data_ptr(), p.M, p.N, p.K,
                                             code, sh)
+        else:
+            st = dg.dg_gemm_fp8_blockscaled_fmt(d["A"].data_ptr(), dg.fmt_code(p.a_fmt), d["sA"].data_ptr(),
+                                                d["B"].data_ptr(), dg.fmt_code(p.b_fmt), d["sB"].data_ptr(),
+                                                d["C"].data_ptr(), p.M, p.N, p.K, code, sh)
         if st != dg.DG_OK:
             raise dg.DGError(st, "bench step")
 
@@ -339,11 +345,15 @@ def main():
 
     cfg = {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "out_dtype": p.out_dtype,
            "scale_block": "128x128", "seed": p.seed, "operand_copies": R}
+    if p.a_fmt != "e4m3" or p.b_fmt != "e4m3":
+        cfg.update({"a_fmt": p.a_fmt, "b_fmt": p.b_fmt})
     if p.grouped:
         cfg.update({"groups": p.G, "real_rows": p.real_rows})
     line = {"metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": K,
             "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+            "scaling": "weak", "vs_baseline": None,
+            "dtype": "fp8_e4m3" if p.a_fmt == p.b_fmt == "e4m3" else f"fp8_{p.a_fmt}x{p.b_fmt}",
+            "data": "synthetic",
             "config": cfg, "roofline": roof, "cpu_baseline": cpu,
             "kernel_ms": round(kern_ms, 5)}
     print(json.dumps(line), flush=True)

@@ -112,6 +112,35 @@ int dg_grouped_gemm_fp8(const void* A, const float* sA,
                         int out_dtype, hipStream_t stream);
 
 typedef enum {
+  DG_FP8_E4M3 = 0,  /* OCP E4M3FN: bias 7, largest finite 448, no infinities */
+  DG_FP8_E5M2 = 1   /* E5M2: bias 15, largest finite 57344, IEEE-style inf/NaN */
+} dg_fp8_format;
+
+/*
+ * The two GEMMs above with a code format per operand (E4M3 and E5M2, the two
+ * FP8 formats of the DeepGEMM FP8 kernel write-up's section 3.1 table; the
+ * FP8-for-MoE page, section 2.1, names both).  dec() of an operand is then
+ * the decode of its format; everything else -- layouts, 128x128 block
+ * scales, per-K-block FP32 rescale, FP32 accumulation, output, errors -- is
+ * as documented for dg_gemm_fp8_blockscaled and dg_grouped_gemm_fp8, which
+ * are these calls with a_fmt = b_fmt = DG_FP8_E4M3.  An unknown format is
+ * DG_ERR_INVALID_ARG.  E5M2 values span 2^-16 .. 57344; products and sums
+ * stay inside FP32, and (as for E4M3) every E5M2 value is an exact FP16
+ * value, so the precision statement is unchanged.  Operands holding E5M2
+ * infinity or NaN codes propagate them.
+ */
+int dg_gemm_fp8_blockscaled_fmt(const void* A, int a_fmt, const float* sA,
+                                const void* B, int b_fmt, const float* sB,
+                                void* C, int64_t M, int64_t N, int64_t K,
+                                int out_dtype, hipStream_t stream);
+
+int dg_grouped_gemm_fp8_fmt(const void* A, int a_fmt, const float* sA,
+                            const void* B, int b_fmt, const float* sB,
+                            void* C, const int32_t* group_offsets,
+                            int num_groups, int64_t M_total, int64_t N, int64_t K,
+                            int out_dtype, hipStream_t stream);
+
+typedef enum {
   DG_IN_F32 = 0,    /* X is float32 */
   DG_IN_BF16 = 1    /* X is bfloat16 */
 } dg_in_dtype;

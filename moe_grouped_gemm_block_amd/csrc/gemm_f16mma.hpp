@@ -50,24 +50,41 @@ namespace dg {
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-// Four E4M3 bytes -> four FP16 values (exact), as two packed pairs.
+// Operand code formats.
+constexpr int FMT_E4M3 = 0;   // OCP E4M3FN
+constexpr int FMT_E5M2 = 1;   // E5M2
+
+// Four FP8 bytes -> four FP16 values (exact), as two packed pairs.  E4M3:
+// the hardware conversion (scale 1).  E5M2: an E5M2 byte is the high byte
+// of the IEEE half of the same value (same sign, 5-bit exponent with bias
+// 15, the first 2 mantissa bits; subnormals, infinities and NaN included),
+// so the conversion only moves bytes.
+template <int FMT = FMT_E4M3>
 __device__ __forceinline__ void fp8x4_to_f16(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(w), 1.0f, false);
-  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(w), 1.0f, true);
-  lo = __builtin_bit_cast(uint32_t, a);
-  hi = __builtin_bit_cast(uint32_t, b);
+  if constexpr (FMT == FMT_E4M3) {
+    const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(w), 1.0f, false);
+    const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(w), 1.0f, true);
+    lo = __builtin_bit_cast(uint32_t, a);
+    hi = __builtin_bit_cast(uint32_t, b);
+  } else {
+    // v_perm_b32 byte selectors (byte 3 .. byte 0 of the result): 0..3 pick
+    // a byte of w, 0x0C gives 0x00
+    lo = __builtin_amdgcn_perm(0u, w, 0x010C000Cu);   // [w.b1, 0, w.b0, 0]
+    hi = __builtin_amdgcn_perm(0u, w, 0x030C020Cu);   // [w.b3, 0, w.b2, 0]
+  }
 }
 
 // 32 FP8 bytes of one fragment row -> the four FP16 MFMA operands of the
 // K-block (operand s holds bytes 8s .. 8s+7).
+template <int FMT = FMT_E4M3>
 __device__ __forceinline__ void fp8x32_to_f16(const int4& r0, const int4& r1, v8h out[4]) {
   const uint32_t w[8] = {uint32_t(r0.x), uint32_t(r0.y), uint32_t(r0.z), uint32_t(r0.w),
                          uint32_t(r1.x), uint32_t(r1.y), uint32_t(r1.z), uint32_t(r1.w)};
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     uint32_t h[4];
-    fp8x4_to_f16(w[2 * s], h[0], h[1]);
-    fp8x4_to_f16(w[2 * s + 1], h[2], h[3]);
+    fp8x4_to_f16<FMT>(w[2 * s], h[0], h[1]);
+    fp8x4_to_f16<FMT>(w[2 * s + 1], h[2], h[3]);
     out[s] = __builtin_bit_cast(v8h, (uint4{h[0], h[1], h[2], h[3]}));
   }
 }
@@ -170,7 +187,7 @@ __device__ __forceinline__ void tile_of(int bid, int m_tiles, int n_tiles, int& 
   tn = r / gsize;
 }
 
-template <int NWM, int NWN, bool OUT_BF16>
+template <int NWM, int NWN, bool OUT_BF16, int FA = FMT_E4M3, int FB = FMT_E4M3>
 __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   constexpr int WM = 64, WN = 128;             // wave sub-tile
   constexpr int MI = WM / 16, NI = WN / 16;    // 16x16 MFMA tiles per wave
@@ -285,7 +302,7 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
     for (int mi = 0; mi < MI; ++mi) {
       const int4 x0 = *reinterpret_cast<const int4*>(la + a_off0 + mi * 16 * KBLK);
       const int4 x1 = *reinterpret_cast<const int4*>(la + a_off1 + mi * 16 * KBLK);
-      fp8x32_to_f16(x0, x1, af[mi]);
+      fp8x32_to_f16<FA>(x0, x1, af[mi]);
     }
     // B column tiles, software-pipelined: while the MFMAs of tile ni consume
     // operand st, operand st of tile ni+1 is converted into the registers
@@ -295,7 +312,7 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
     int4 y0 = *reinterpret_cast<const int4*>(lb + b_off0);
     int4 y1 = *reinterpret_cast<const int4*>(lb + b_off1);
     v8h bf[4];
-    fp8x32_to_f16(y0, y1, bf);
+    fp8x32_to_f16<FB>(y0, y1, bf);
     if (NI > 1) {
       y0 = *reinterpret_cast<const int4*>(lb + b_off0 + 16 * KBLK);
       y1 = *reinterpret_cast<const int4*>(lb + b_off1 + 16 * KBLK);
@@ -319,8 +336,8 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
           const int4& y = st < 2 ? y0 : y1;
           const uint32_t w0 = uint32_t((st & 1) ? y.z : y.x), w1 = uint32_t((st & 1) ? y.w : y.y);
           uint32_t h[4];
-          fp8x4_to_f16(w0, h[0], h[1]);
-          fp8x4_to_f16(w1, h[2], h[3]);
+          fp8x4_to_f16<FB>(w0, h[0], h[1]);
+          fp8x4_to_f16<FB>(w1, h[2], h[3]);
           bf[st] = __builtin_bit_cast(v8h, (uint4{h[0], h[1], h[2], h[3]}));
           if (ni + 2 < NI && st == 1)
             y0 = *reinterpret_cast<const int4*>(lb + b_off0 + (ni + 2) * 16 * KBLK);
@@ -401,16 +418,26 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
 }
 
 // Named kernels (one per tile shape and output type) around the body.
-#define DG_GEMM_KERNEL(NAME, NWM, NWN, BF16)                              \
-  __global__ __launch_bounds__(64 * NWM * NWN, 1) void NAME(GemmArgs p) { \
-    gemm_f16mma_body<NWM, NWN, BF16>(p);                                  \
+// One named kernel per tile shape, output type and pair of operand formats
+// (suffix _a<A format>b<B format>, 4 = E4M3, 5 = E5M2; E4M3 x E4M3 keeps the
+// plain name).
+#define DG_GEMM_KERNEL(NAME, NWM, NWN, BF16, FA, FB)                        \
+  __global__ __launch_bounds__(64 * NWM * NWN, 1) void NAME(GemmArgs p) {   \
+    gemm_f16mma_body<NWM, NWN, BF16, FA, FB>(p);                            \
   }
-DG_GEMM_KERNEL(dg_gemm_128x512_bf16, 2, 4, true)
-DG_GEMM_KERNEL(dg_gemm_128x512_f32, 2, 4, false)
-DG_GEMM_KERNEL(dg_gemm_128x256_bf16, 2, 2, true)
-DG_GEMM_KERNEL(dg_gemm_128x256_f32, 2, 2, false)
-DG_GEMM_KERNEL(dg_gemm_128x128_bf16, 2, 1, true)
-DG_GEMM_KERNEL(dg_gemm_128x128_f32, 2, 1, false)
+#define DG_GEMM_SHAPE(SHAPE, NWM, NWN, SFX, FA, FB)                         \
+  DG_GEMM_KERNEL(dg_gemm_##SHAPE##_bf16##SFX, NWM, NWN, true, FA, FB)       \
+  DG_GEMM_KERNEL(dg_gemm_##SHAPE##_f32##SFX, NWM, NWN, false, FA, FB)
+#define DG_GEMM_FORMATS(SFX, FA, FB)                                        \
+  DG_GEMM_SHAPE(128x512, 2, 4, SFX, FA, FB)                                 \
+  DG_GEMM_SHAPE(128x256, 2, 2, SFX, FA, FB)                                 \
+  DG_GEMM_SHAPE(128x128, 2, 1, SFX, FA, FB)
+DG_GEMM_FORMATS(, FMT_E4M3, FMT_E4M3)
+DG_GEMM_FORMATS(_a5b5, FMT_E5M2, FMT_E5M2)
+DG_GEMM_FORMATS(_a4b5, FMT_E4M3, FMT_E5M2)
+DG_GEMM_FORMATS(_a5b4, FMT_E5M2, FMT_E4M3)
+#undef DG_GEMM_FORMATS
+#undef DG_GEMM_SHAPE
 #undef DG_GEMM_KERNEL
 
 }  // namespace dg

@@ -23,7 +23,7 @@
 
 namespace dg {
 
-template <int MI, int NI, bool OUT_BF16>
+template <int MI, int NI, bool OUT_BF16, int FA = FMT_E4M3, int FB = FMT_E4M3>
 __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p) {
   constexpr int NW = 4;                         // waves, each a quarter of the K-blocks
   constexpr int RM = 16 * MI, CN = 16 * NI;     // rows / columns of the workgroup tile
@@ -118,14 +118,14 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p) {
     for (int mi = 0; mi < MI; ++mi) {
       const int4 x0 = *reinterpret_cast<const int4*>(la + off0 + mi * 16 * KBLK);
       const int4 x1 = *reinterpret_cast<const int4*>(la + off1 + mi * 16 * KBLK);
-      fp8x32_to_f16(x0, x1, af[mi]);
+      fp8x32_to_f16<FA>(x0, x1, af[mi]);
     }
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       const int4 y0 = *reinterpret_cast<const int4*>(lb + off0 + ni * 16 * KBLK);
       const int4 y1 = *reinterpret_cast<const int4*>(lb + off1 + ni * 16 * KBLK);
       v8h bf[4];
-      fp8x32_to_f16(y0, y1, bf);
+      fp8x32_to_f16<FB>(y0, y1, bf);
       const float s = sa * sb[ni];
       v4f part[MI];
 #pragma unroll
@@ -183,20 +183,21 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p) {
   }
 }
 
-#define DG_SKINNY_KERNEL(NAME, MI, NI, BF16) \
-  __global__ __launch_bounds__(256, 1) void NAME(GemmArgs p) { gemm_skinny_body<MI, NI, BF16>(p); }
-DG_SKINNY_KERNEL(dg_skinny_m64_n48_bf16, 4, 3, true)
-DG_SKINNY_KERNEL(dg_skinny_m64_n48_f32, 4, 3, false)
-DG_SKINNY_KERNEL(dg_skinny_m64_n16_bf16, 4, 1, true)
-DG_SKINNY_KERNEL(dg_skinny_m64_n16_f32, 4, 1, false)
-DG_SKINNY_KERNEL(dg_skinny_m32_n48_bf16, 2, 3, true)
-DG_SKINNY_KERNEL(dg_skinny_m32_n48_f32, 2, 3, false)
-DG_SKINNY_KERNEL(dg_skinny_m32_n16_bf16, 2, 1, true)
-DG_SKINNY_KERNEL(dg_skinny_m32_n16_f32, 2, 1, false)
-DG_SKINNY_KERNEL(dg_skinny_m16_n48_bf16, 1, 3, true)
-DG_SKINNY_KERNEL(dg_skinny_m16_n48_f32, 1, 3, false)
-DG_SKINNY_KERNEL(dg_skinny_m16_n16_bf16, 1, 1, true)
-DG_SKINNY_KERNEL(dg_skinny_m16_n16_f32, 1, 1, false)
+#define DG_SKINNY_KERNEL(NAME, MI, NI, BF16, FA, FB) \
+  __global__ __launch_bounds__(256, 1) void NAME(GemmArgs p) { gemm_skinny_body<MI, NI, BF16, FA, FB>(p); }
+#define DG_SKINNY_SHAPE(ROWS, COLS, MI, NI, SFX, FA, FB)                                \
+  DG_SKINNY_KERNEL(dg_skinny_m##ROWS##_n##COLS##_bf16##SFX, MI, NI, true, FA, FB)       \
+  DG_SKINNY_KERNEL(dg_skinny_m##ROWS##_n##COLS##_f32##SFX, MI, NI, false, FA, FB)
+#define DG_SKINNY_FORMATS(SFX, FA, FB)                                                  \
+  DG_SKINNY_SHAPE(64, 48, 4, 3, SFX, FA, FB) DG_SKINNY_SHAPE(64, 16, 4, 1, SFX, FA, FB) \
+  DG_SKINNY_SHAPE(32, 48, 2, 3, SFX, FA, FB) DG_SKINNY_SHAPE(32, 16, 2, 1, SFX, FA, FB) \
+  DG_SKINNY_SHAPE(16, 48, 1, 3, SFX, FA, FB) DG_SKINNY_SHAPE(16, 16, 1, 1, SFX, FA, FB)
+DG_SKINNY_FORMATS(, FMT_E4M3, FMT_E4M3)
+DG_SKINNY_FORMATS(_a5b5, FMT_E5M2, FMT_E5M2)
+DG_SKINNY_FORMATS(_a4b5, FMT_E4M3, FMT_E5M2)
+DG_SKINNY_FORMATS(_a5b4, FMT_E5M2, FMT_E4M3)
+#undef DG_SKINNY_FORMATS
+#undef DG_SKINNY_SHAPE
 #undef DG_SKINNY_KERNEL
 
 }  // namespace dg

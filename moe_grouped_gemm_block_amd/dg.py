@@ -21,13 +21,15 @@ DG_OUT_F32 = 0
 DG_OUT_BF16 = 1
 DG_IN_F32 = 0
 DG_IN_BF16 = 1
+DG_FP8_E4M3 = 0
+DG_FP8_E5M2 = 1
 DG_OK = 0
 DG_ERR_INVALID_ARG = -1
 DG_ERR_UNSUPPORTED = -2
 DG_ERR_LAUNCH = -3
 
-EXPORTED = ("dg_gemm_fp8_blockscaled", "dg_grouped_gemm_fp8", "dg_quantize_fp8_blockscaled",
-            "dg_status_string")
+EXPORTED = ("dg_gemm_fp8_blockscaled", "dg_grouped_gemm_fp8", "dg_gemm_fp8_blockscaled_fmt",
+            "dg_grouped_gemm_fp8_fmt", "dg_quantize_fp8_blockscaled", "dg_status_string")
 
 _lib = None
 
@@ -46,6 +48,10 @@ def lib() -> ctypes.CDLL:
         L.dg_gemm_fp8_blockscaled.restype = ci
         L.dg_grouped_gemm_fp8.argtypes = [vp, vp, vp, vp, vp, vp, ci, i64, i64, i64, ci, vp]
         L.dg_grouped_gemm_fp8.restype = ci
+        L.dg_gemm_fp8_blockscaled_fmt.argtypes = [vp, ci, vp, vp, ci, vp, vp, i64, i64, i64, ci, vp]
+        L.dg_gemm_fp8_blockscaled_fmt.restype = ci
+        L.dg_grouped_gemm_fp8_fmt.argtypes = [vp, ci, vp, vp, ci, vp, vp, vp, ci, i64, i64, i64, ci, vp]
+        L.dg_grouped_gemm_fp8_fmt.restype = ci
         L.dg_quantize_fp8_blockscaled.argtypes = [vp, ci, vp, vp, i64, i64, ci, vp]
         L.dg_quantize_fp8_blockscaled.restype = ci
         L.dg_status_string.argtypes = [ci]
@@ -64,6 +70,16 @@ def dg_grouped_gemm_fp8(A, sA, B, sB, C, group_offsets, num_groups, M_total, N, 
                         out_dtype, stream) -> int:
     return lib().dg_grouped_gemm_fp8(A, sA, B, sB, C, group_offsets, num_groups, M_total,
                                      N, K, out_dtype, stream)
+
+
+def dg_gemm_fp8_blockscaled_fmt(A, a_fmt, sA, B, b_fmt, sB, C, M, N, K, out_dtype, stream) -> int:
+    return lib().dg_gemm_fp8_blockscaled_fmt(A, a_fmt, sA, B, b_fmt, sB, C, M, N, K, out_dtype, stream)
+
+
+def dg_grouped_gemm_fp8_fmt(A, a_fmt, sA, B, b_fmt, sB, C, group_offsets, num_groups, M_total, N, K,
+                            out_dtype, stream) -> int:
+    return lib().dg_grouped_gemm_fp8_fmt(A, a_fmt, sA, B, b_fmt, sB, C, group_offsets, num_groups,
+                                         M_total, N, K, out_dtype, stream)
 
 
 def dg_quantize_fp8_blockscaled(X, in_dtype, Q, S, M, K, block_rows, stream) -> int:
@@ -89,8 +105,8 @@ def _torch():
 
 def _check_fp8(t, name):
     torch = _torch()
-    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
-        raise TypeError(f"{name} must be uint8 E4M3 codes or float8_e4m3fn, got {t.dtype}")
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn, torch.float8_e5m2):
+        raise TypeError(f"{name} must be uint8 FP8 codes, float8_e4m3fn or float8_e5m2, got {t.dtype}")
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous device tensor")
 
@@ -121,14 +137,23 @@ def out_code(out_dtype) -> int:
     raise ValueError(f"unknown out_dtype {out_dtype!r}")
 
 
+def fmt_code(fmt) -> int:
+    if fmt in (DG_FP8_E4M3, "e4m3"):
+        return DG_FP8_E4M3
+    if fmt in (DG_FP8_E5M2, "e5m2"):
+        return DG_FP8_E5M2
+    raise ValueError(f"unknown FP8 format {fmt!r}")
+
+
 def _stream(stream):
     if stream is None:
         return _torch().cuda.current_stream().cuda_stream
     return getattr(stream, "cuda_stream", stream)
 
 
-def gemm_fp8_blockscaled(A, sA, B, sB, out_dtype="bf16", C=None, stream=None):
-    """C[M][N] = block-scaled A[M][K] x B (stored [N][K]) on the device."""
+def gemm_fp8_blockscaled(A, sA, B, sB, out_dtype="bf16", C=None, stream=None, a_fmt="e4m3", b_fmt="e4m3"):
+    """C[M][N] = block-scaled A[M][K] x B (stored [N][K]) on the device; the
+    operands' FP8 formats are "e4m3" (default) or "e5m2"."""
     _check_fp8(A, "A")
     _check_fp8(B, "B")
     M, K = A.shape
@@ -139,14 +164,20 @@ def gemm_fp8_blockscaled(A, sA, B, sB, out_dtype="bf16", C=None, stream=None):
     _check_f32(sB, "sB", (-(-N // 128), K // 128))
     code = out_code(out_dtype)
     C = _out(C, M, N, code, A)
-    st = dg_gemm_fp8_blockscaled(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(),
-                                 C.data_ptr(), M, N, K, code, _stream(stream))
+    fa, fb = fmt_code(a_fmt), fmt_code(b_fmt)
+    if fa == DG_FP8_E4M3 and fb == DG_FP8_E4M3:
+        st = dg_gemm_fp8_blockscaled(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(),
+                                     C.data_ptr(), M, N, K, code, _stream(stream))
+    else:
+        st = dg_gemm_fp8_blockscaled_fmt(A.data_ptr(), fa, sA.data_ptr(), B.data_ptr(), fb, sB.data_ptr(),
+                                         C.data_ptr(), M, N, K, code, _stream(stream))
     if st != DG_OK:
         raise DGError(st, "dg_gemm_fp8_blockscaled")
     return C
 
 
-def grouped_gemm_fp8(A, sA, B, sB, group_offsets, out_dtype="bf16", C=None, stream=None):
+def grouped_gemm_fp8(A, sA, B, sB, group_offsets, out_dtype="bf16", C=None, stream=None,
+                     a_fmt="e4m3", b_fmt="e4m3"):
     """MoE grouped GEMM over contiguous 128-row-padded expert segments."""
     torch = _torch()
     _check_fp8(A, "A")
@@ -162,9 +193,15 @@ def grouped_gemm_fp8(A, sA, B, sB, group_offsets, out_dtype="bf16", C=None, stre
         raise ValueError("group_offsets must be a device int32 tensor of G + 1 entries")
     code = out_code(out_dtype)
     C = _out(C, M_total, N, code, A)
-    st = dg_grouped_gemm_fp8(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(),
-                             C.data_ptr(), group_offsets.data_ptr(), G, M_total, N, K, code,
-                             _stream(stream))
+    fa, fb = fmt_code(a_fmt), fmt_code(b_fmt)
+    if fa == DG_FP8_E4M3 and fb == DG_FP8_E4M3:
+        st = dg_grouped_gemm_fp8(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(),
+                                 C.data_ptr(), group_offsets.data_ptr(), G, M_total, N, K, code,
+                                 _stream(stream))
+    else:
+        st = dg_grouped_gemm_fp8_fmt(A.data_ptr(), fa, sA.data_ptr(), B.data_ptr(), fb, sB.data_ptr(),
+                                     C.data_ptr(), group_offsets.data_ptr(), G, M_total, N, K, code,
+                                     _stream(stream))
     if st != DG_OK:
         raise DGError(st, "dg_grouped_gemm_fp8")
     return C

@@ -308,17 +308,24 @@ CONFIG_NAMES = {
 }
 
 
-def make_config(i: int, seed: int | None = None) -> Problem:
-    """Workload i (1..5); the default seed is the workload index."""
+def make_config(i: int, seed: int | None = None, fmt: str = "e4m3") -> Problem:
+    """Workload i (1..5); the default seed is the workload index.  fmt =
+    "e5m2" quantises both operands of the dense workloads 1-3 to E5M2
+    instead (same data, name suffixed with _e5m2)."""
     s = i if seed is None else seed
+    if fmt != "e4m3" and i > 3:
+        raise ValueError("E5M2 variants exist for the dense workloads 1-3")
+    sfx = "" if fmt == "e4m3" else f"_{fmt}"
     if i == 1:
-        return dense_problem(256, 256, 256, s, out_dtype="f32", name=CONFIG_NAMES[1])
+        return dense_problem(256, 256, 256, s, out_dtype="f32", name=CONFIG_NAMES[1] + sfx,
+                             a_fmt=fmt, b_fmt=fmt)
     if i == 2:
         return dense_problem(4096, 4096, 4096, s, out_dtype="bf16",
-                             block_log2_range=4.0, name=CONFIG_NAMES[2])
+                             block_log2_range=4.0, name=CONFIG_NAMES[2] + sfx, a_fmt=fmt, b_fmt=fmt)
     if i == 3:
         return dense_problem(64, 12288, 4096, s, out_dtype="bf16", b_std=0.02,
-                             outlier_frac=0.01, outlier_mult=50.0, name=CONFIG_NAMES[3])
+                             outlier_frac=0.01, outlier_mult=50.0, name=CONFIG_NAMES[3] + sfx,
+                             a_fmt=fmt, b_fmt=fmt)
     if i == 4:
         return grouped_problem(8, 4096, 4096, 4096, s, popularity="uniform",
                                name=CONFIG_NAMES[4])
