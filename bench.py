@@ -99,9 +99,10 @@ def cpu_baseline(p, target_s: float = 12.0):
     def run(rows):
         t = time.perf_counter()
         if p.grouped:
-            oracle.grouped_gemm(p.A, p.sA, p.B, p.sB, p.group_offsets, rows=rows)
+            oracle.grouped_gemm(p.A, p.sA, p.B, p.sB, p.group_offsets, rows=rows, sa_rows=p.sa_rows)
         else:
-            oracle.gemm_blockscaled(p.A, p.sA, p.B, p.sB, rows=rows, a_fmt=p.a_fmt, b_fmt=p.b_fmt)
+            oracle.gemm_blockscaled(p.A, p.sA, p.B, p.sB, rows=rows, a_fmt=p.a_fmt, b_fmt=p.b_fmt,
+                                    sa_rows=p.sa_rows)
         return time.perf_counter() - t
 
     calib = np.sort(rng.choice(M, size=min(M, 64), replace=False))
@@ -214,6 +215,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="operand copies (0 = enough to exceed the Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--op", choices=["gemm", "quantize"], default="gemm")
+    ap.add_argument("--a-scale", choices=["128x128", "1x128"], default="128x128",
+                    help="A scale blocks of the GEMM: 128x128, or one per token and 128 columns")
     ap.add_argument("--fmt", choices=["e4m3", "e5m2"], default="e4m3",
                     help="operand FP8 format of the dense workloads 1-3 (both operands)")
     ap.add_argument("--block-rows", type=int, default=128, choices=[1, 128],
@@ -255,7 +258,7 @@ def main():
     dg.lib()
 
     t0 = time.perf_counter()
-    p = I.make_config(args.workload, fmt=args.fmt)
+    p = I.make_config(args.workload, fmt=args.fmt, sa_rows=1 if args.a_scale == "1x128" else 128)
     log(f"generated {p.name} in {time.perf_counter() - t0:.1f}s: M={p.M} N={p.N} K={p.K} "
         f"G={p.G} real_rows={p.real_rows}")
 
@@ -278,18 +281,24 @@ def main():
 
     def step(i):
         d = copies[i % R]
-        if p.grouped:
+        plain = p.a_fmt == "e4m3" and p.b_fmt == "e4m3" and p.sa_rows == 128
+        fa, fb = dg.fmt_code(p.a_fmt), dg.fmt_code(p.b_fmt)
+        if p.grouped and plain:
             st = dg.dg_grouped_gemm_fp8(d["A"].data_ptr(), d["sA"].data_ptr(), d["B"].data_ptr(),
                                         d["sB"].data_ptr(), d["C"].data_ptr(), d["offs"].data_ptr(),
                                         p.G, p.M, p.N, p.K, code, sh)
-        elif p.a_fmt == "e4m3" and p.b_fmt == "e4m3":
+        elif p.grouped:
+            st = dg.dg_grouped_gemm_fp8_ex(d["A"].data_ptr(), fa, d["sA"].data_ptr(), p.sa_rows,
+                                           d["B"].data_ptr(), fb, d["sB"].data_ptr(), d["C"].data_ptr(),
+                                           d["offs"].data_ptr(), p.G, p.M, p.N, p.K, code, sh)
+        elif plain:
             st = dg.dg_gemm_fp8_blockscaled(d["A"].data_ptr(), d["sA"].data_ptr(), d["B"].data_ptr(),
                                             d["sB"].data_ptr(), d["C"].data_ptr(), p.M, p.N, p.K,
                                             code, sh)
         else:
-            st = dg.dg_gemm_fp8_blockscaled_fmt(d["A"].data_ptr(), dg.fmt_code(p.a_fmt), d["sA"].data_ptr(),
-                                                d["B"].data_ptr(), dg.fmt_code(p.b_fmt), d["sB"].data_ptr(),
-                                                d["C"].data_ptr(), p.M, p.N, p.K, code, sh)
+            st = dg.dg_gemm_fp8_ex(d["A"].data_ptr(), fa, d["sA"].data_ptr(), p.sa_rows,
+                                   d["B"].data_ptr(), fb, d["sB"].data_ptr(),
+                                   d["C"].data_ptr(), p.M, p.N, p.K, code, sh)
         if st != dg.DG_OK:
             raise dg.DGError(st, "bench step")
 
@@ -344,7 +353,8 @@ def main():
         log(f"cpu oracle: {cpu}")
 
     cfg = {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "out_dtype": p.out_dtype,
-           "scale_block": "128x128", "seed": p.seed, "operand_copies": R}
+           "scale_block": "128x128" if p.sa_rows == 128 else "A 1x128, B 128x128", "seed": p.seed,
+           "operand_copies": R}
     if p.a_fmt != "e4m3" or p.b_fmt != "e4m3":
         cfg.update({"a_fmt": p.a_fmt, "b_fmt": p.b_fmt})
     if p.grouped:

@@ -117,28 +117,40 @@ typedef enum {
 } dg_fp8_format;
 
 /*
- * The two GEMMs above with a code format per operand (E4M3 and E5M2, the two
- * FP8 formats of the DeepGEMM FP8 kernel write-up's section 3.1 table; the
- * FP8-for-MoE page, section 2.1, names both).  dec() of an operand is then
- * the decode of its format; everything else -- layouts, 128x128 block
- * scales, per-K-block FP32 rescale, FP32 accumulation, output, errors -- is
- * as documented for dg_gemm_fp8_blockscaled and dg_grouped_gemm_fp8, which
- * are these calls with a_fmt = b_fmt = DG_FP8_E4M3.  An unknown format is
- * DG_ERR_INVALID_ARG.  E5M2 values span 2^-16 .. 57344; products and sums
- * stay inside FP32, and (as for E4M3) every E5M2 value is an exact FP16
- * value, so the precision statement is unchanged.  Operands holding E5M2
- * infinity or NaN codes propagate them.
+ * The two GEMMs above, generalised in two ways:
+ *
+ *   a_fmt, b_fmt : the code format of each operand (E4M3 and E5M2, the two
+ *                  FP8 formats of the DeepGEMM FP8 kernel write-up's section
+ *                  3.1 table; the FP8-for-MoE page, section 2.1, names both).
+ *                  dec() of an operand is the decode of its format.  E5M2
+ *                  values span 2^-16 .. 57344 and, like E4M3, are exact FP16
+ *                  values, so the precision statement is unchanged; E5M2
+ *                  infinity and NaN codes propagate.
+ *   sa_rows      : rows per A scale block, 128 or 1.  128 is the 128 x 128
+ *                  layout above.  1 gives every row (token) its own scale per
+ *                  128-wide K-block, the 1 x 128 granularity of the FP8 kernel
+ *                  write-up's section 5.2 table, which
+ *                  dg_quantize_fp8_blockscaled(block_rows = 1) produces:
+ *                    sA : float32 [M][K/128] row-major (grouped: [M_total][K/128])
+ *                  and C[i][j] takes fp32(sA[i][kb] * sB[j/128][kb]) as the
+ *                  factor of P_kb[i][j].  B keeps its 128 x 128 blocks.
+ *
+ * Everything else -- layouts, per-K-block FP32 rescale, FP32 accumulation,
+ * output, errors -- is as documented for dg_gemm_fp8_blockscaled and
+ * dg_grouped_gemm_fp8, which are these calls with a_fmt = b_fmt =
+ * DG_FP8_E4M3 and sa_rows = 128.  An unknown format or an sa_rows other than
+ * 1 or 128 is DG_ERR_INVALID_ARG.
  */
-int dg_gemm_fp8_blockscaled_fmt(const void* A, int a_fmt, const float* sA,
-                                const void* B, int b_fmt, const float* sB,
-                                void* C, int64_t M, int64_t N, int64_t K,
-                                int out_dtype, hipStream_t stream);
+int dg_gemm_fp8_ex(const void* A, int a_fmt, const float* sA, int sa_rows,
+                   const void* B, int b_fmt, const float* sB,
+                   void* C, int64_t M, int64_t N, int64_t K,
+                   int out_dtype, hipStream_t stream);
 
-int dg_grouped_gemm_fp8_fmt(const void* A, int a_fmt, const float* sA,
-                            const void* B, int b_fmt, const float* sB,
-                            void* C, const int32_t* group_offsets,
-                            int num_groups, int64_t M_total, int64_t N, int64_t K,
-                            int out_dtype, hipStream_t stream);
+int dg_grouped_gemm_fp8_ex(const void* A, int a_fmt, const float* sA, int sa_rows,
+                           const void* B, int b_fmt, const float* sB,
+                           void* C, const int32_t* group_offsets,
+                           int num_groups, int64_t M_total, int64_t N, int64_t K,
+                           int out_dtype, hipStream_t stream);
 
 typedef enum {
   DG_IN_F32 = 0,    /* X is float32 */

@@ -84,45 +84,59 @@ int launch_tiles(dg::GemmArgs a, int bn, int threads, void (*k_bf16)(dg::GemmArg
 
 typedef void (*kfn)(dg::GemmArgs);
 
-// Kernels of one pair of operand formats; combo = 2 * a_fmt + b_fmt.
-struct TiledSet { kfn k512[2], k256[2], k128[2]; };   // [f32, bf16]
+// Kernels of one pair of operand formats; combo = 2 * a_fmt + b_fmt.  The
+// *rs kernels take one A scale per row (1 x 128 blocks).
+struct TiledSet { kfn k512[2], k256[2], k128[2], k256rs[2], k128rs[2]; };   // [f32, bf16]
 #define DG_TILED_SET(SFX)                                                   \
   {{dg::dg_gemm_128x512_f32##SFX, dg::dg_gemm_128x512_bf16##SFX},           \
    {dg::dg_gemm_128x256_f32##SFX, dg::dg_gemm_128x256_bf16##SFX},           \
-   {dg::dg_gemm_128x128_f32##SFX, dg::dg_gemm_128x128_bf16##SFX}}
+   {dg::dg_gemm_128x128_f32##SFX, dg::dg_gemm_128x128_bf16##SFX},           \
+   {dg::dg_gemm_128x256_f32##SFX##_rs, dg::dg_gemm_128x256_bf16##SFX##_rs}, \
+   {dg::dg_gemm_128x128_f32##SFX##_rs, dg::dg_gemm_128x128_bf16##SFX##_rs}}
 const TiledSet kTiled[4] = {DG_TILED_SET(), DG_TILED_SET(_a4b5), DG_TILED_SET(_a5b4), DG_TILED_SET(_a5b5)};
 #undef DG_TILED_SET
 
-// [rows 16/32/64][NI 1/3][f32/bf16]
-struct SkinnySet { kfn t[3][2][2]; };
-#define DG_SKINNY_SET(SFX)                                                                                  \
-  {{{{dg::dg_skinny_m16_n16_f32##SFX, dg::dg_skinny_m16_n16_bf16##SFX},                                    \
-     {dg::dg_skinny_m16_n48_f32##SFX, dg::dg_skinny_m16_n48_bf16##SFX}},                                   \
-    {{dg::dg_skinny_m32_n16_f32##SFX, dg::dg_skinny_m32_n16_bf16##SFX},                                    \
-     {dg::dg_skinny_m32_n48_f32##SFX, dg::dg_skinny_m32_n48_bf16##SFX}},                                   \
-    {{dg::dg_skinny_m64_n16_f32##SFX, dg::dg_skinny_m64_n16_bf16##SFX},                                    \
-     {dg::dg_skinny_m64_n48_f32##SFX, dg::dg_skinny_m64_n48_bf16##SFX}}}}
+// [A scales per block / per row][rows 16/32/64][NI 1/3][f32/bf16]
+struct SkinnySet { kfn t[2][3][2][2]; };
+#define DG_SKINNY_ROWS(SFX)                                                                                 \
+  {{{dg::dg_skinny_m16_n16_f32##SFX, dg::dg_skinny_m16_n16_bf16##SFX},                                     \
+    {dg::dg_skinny_m16_n48_f32##SFX, dg::dg_skinny_m16_n48_bf16##SFX}},                                    \
+   {{dg::dg_skinny_m32_n16_f32##SFX, dg::dg_skinny_m32_n16_bf16##SFX},                                     \
+    {dg::dg_skinny_m32_n48_f32##SFX, dg::dg_skinny_m32_n48_bf16##SFX}},                                    \
+   {{dg::dg_skinny_m64_n16_f32##SFX, dg::dg_skinny_m64_n16_bf16##SFX},                                     \
+    {dg::dg_skinny_m64_n48_f32##SFX, dg::dg_skinny_m64_n48_bf16##SFX}}}
+#define DG_SKINNY_SET(SFX) {{DG_SKINNY_ROWS(SFX), DG_SKINNY_ROWS(SFX##_rs)}}
 const SkinnySet kSkinny[4] = {DG_SKINNY_SET(), DG_SKINNY_SET(_a4b5), DG_SKINNY_SET(_a5b4), DG_SKINNY_SET(_a5b5)};
 #undef DG_SKINNY_SET
+#undef DG_SKINNY_ROWS
 
 // Few rows (M <= 64, dense): one workgroup per 16*NI columns, its four waves
 // splitting K; NI = 3 once that still gives every CU a workgroup.
-int launch_skinny(dg::GemmArgs a, int out_dtype, int combo, hipStream_t stream) {
+int launch_skinny(dg::GemmArgs a, int out_dtype, int combo, int row_sa, hipStream_t stream) {
   const int rows = a.M <= 16 ? 0 : a.M <= 32 ? 1 : 2;
   const int wide = int64_t(a.N) >= int64_t(48) * kCUs ? 1 : 0;
   const int cols = wide ? 48 : 16;
   const int64_t blocks = (int64_t(a.N) + cols - 1) / cols;
   if (blocks > INT32_MAX) return DG_ERR_UNSUPPORTED;
   void* kargs[] = {&a};
-  const void* fn = reinterpret_cast<const void*>(kSkinny[combo].t[rows][wide][out_dtype == DG_OUT_BF16 ? 1 : 0]);
+  const void* fn =
+      reinterpret_cast<const void*>(kSkinny[combo].t[row_sa][rows][wide][out_dtype == DG_OUT_BF16 ? 1 : 0]);
   hipError_t err = hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(256), kargs, 0, stream);
   return err == hipSuccess ? DG_OK : DG_ERR_LAUNCH;
 }
 
-int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, hipStream_t stream) {
+int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, int row_sa, hipStream_t stream) {
   const int combo = 2 * a_fmt + b_fmt;
   const TiledSet& ks = kTiled[combo];
-  if (a.offs == nullptr && a.M <= 64 && forced_tile() == 0) return launch_skinny(a, out_dtype, combo, stream);
+  if (a.offs == nullptr && a.M <= 64 && forced_tile() == 0)
+    return launch_skinny(a, out_dtype, combo, row_sa, stream);
+  if (row_sa) {
+    // Per-row A scales need a small LDS stage next to the A and B stages,
+    // which the 160 KB of the 128 x 512 tile leave no room for.
+    if (forced_tile() == 128 || a.N <= 128)
+      return launch_tiles(a, 128, 128, ks.k128rs[1], ks.k128rs[0], out_dtype, stream);
+    return launch_tiles(a, 256, 256, ks.k256rs[1], ks.k256rs[0], out_dtype, stream);
+  }
   const int64_t m_tiles = (int64_t(a.M) + 127) / 128;
   const int64_t wide = m_tiles * ((int64_t(a.N) + 511) / 512);
   bool use512 = a.N > 256 && wide >= kCUs / 2;
@@ -156,9 +170,10 @@ int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, hipStream
 
 bool valid_fmt(int f) { return f == DG_FP8_E4M3 || f == DG_FP8_E5M2; }
 
-int gemm_impl(const void* A, int a_fmt, const float* sA, const void* B, int b_fmt, const float* sB,
-              void* C, int64_t M, int64_t N, int64_t K, int out_dtype, hipStream_t stream) {
+int gemm_impl(const void* A, int a_fmt, const float* sA, int sa_rows, const void* B, int b_fmt,
+              const float* sB, void* C, int64_t M, int64_t N, int64_t K, int out_dtype, hipStream_t stream) {
   if (!valid_fmt(a_fmt) || !valid_fmt(b_fmt)) return DG_ERR_INVALID_ARG;
+  if (sa_rows != 128 && sa_rows != 1) return DG_ERR_INVALID_ARG;
   int st = check_common(A, sA, B, sB, C, M, N, K, out_dtype);
   if (st != DG_OK || M == 0 || N == 0) return st;
   dg::GemmArgs a{};
@@ -172,13 +187,14 @@ int gemm_impl(const void* A, int a_fmt, const float* sA, const void* B, int b_fm
   a.M = int(M);
   a.N = int(N);
   a.K = int(K);
-  return launch(a, out_dtype, a_fmt, b_fmt, stream);
+  return launch(a, out_dtype, a_fmt, b_fmt, sa_rows == 1, stream);
 }
 
-int grouped_impl(const void* A, int a_fmt, const float* sA, const void* B, int b_fmt, const float* sB,
-                 void* C, const int32_t* group_offsets, int num_groups, int64_t M_total, int64_t N,
-                 int64_t K, int out_dtype, hipStream_t stream) {
+int grouped_impl(const void* A, int a_fmt, const float* sA, int sa_rows, const void* B, int b_fmt,
+                 const float* sB, void* C, const int32_t* group_offsets, int num_groups, int64_t M_total,
+                 int64_t N, int64_t K, int out_dtype, hipStream_t stream) {
   if (!valid_fmt(a_fmt) || !valid_fmt(b_fmt)) return DG_ERR_INVALID_ARG;
+  if (sa_rows != 128 && sa_rows != 1) return DG_ERR_INVALID_ARG;
   if (num_groups < 1) return DG_ERR_INVALID_ARG;
   if (M_total < 0 || M_total % dg::KBLK != 0) return DG_ERR_INVALID_ARG;
   int st = check_common(A, sA, B, sB, C, M_total, N, K, out_dtype);
@@ -195,7 +211,7 @@ int grouped_impl(const void* A, int a_fmt, const float* sA, const void* B, int b
   a.M = int(M_total);
   a.N = int(N);
   a.K = int(K);
-  return launch(a, out_dtype, a_fmt, b_fmt, stream);
+  return launch(a, out_dtype, a_fmt, b_fmt, sa_rows == 1, stream);
 }
 
 }  // namespace
@@ -205,27 +221,27 @@ extern "C" {
 int dg_gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const float* sB,
                             void* C, int64_t M, int64_t N, int64_t K, int out_dtype,
                             hipStream_t stream) {
-  return gemm_impl(A, DG_FP8_E4M3, sA, B, DG_FP8_E4M3, sB, C, M, N, K, out_dtype, stream);
+  return gemm_impl(A, DG_FP8_E4M3, sA, 128, B, DG_FP8_E4M3, sB, C, M, N, K, out_dtype, stream);
 }
 
 int dg_grouped_gemm_fp8(const void* A, const float* sA, const void* B, const float* sB, void* C,
                         const int32_t* group_offsets, int num_groups, int64_t M_total,
                         int64_t N, int64_t K, int out_dtype, hipStream_t stream) {
-  return grouped_impl(A, DG_FP8_E4M3, sA, B, DG_FP8_E4M3, sB, C, group_offsets, num_groups, M_total, N, K,
+  return grouped_impl(A, DG_FP8_E4M3, sA, 128, B, DG_FP8_E4M3, sB, C, group_offsets, num_groups, M_total, N,
+                      K, out_dtype, stream);
+}
+
+int dg_gemm_fp8_ex(const void* A, int a_fmt, const float* sA, int sa_rows, const void* B, int b_fmt,
+                   const float* sB, void* C, int64_t M, int64_t N, int64_t K, int out_dtype,
+                   hipStream_t stream) {
+  return gemm_impl(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, M, N, K, out_dtype, stream);
+}
+
+int dg_grouped_gemm_fp8_ex(const void* A, int a_fmt, const float* sA, int sa_rows, const void* B, int b_fmt,
+                           const float* sB, void* C, const int32_t* group_offsets, int num_groups,
+                           int64_t M_total, int64_t N, int64_t K, int out_dtype, hipStream_t stream) {
+  return grouped_impl(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, group_offsets, num_groups, M_total, N, K,
                       out_dtype, stream);
-}
-
-int dg_gemm_fp8_blockscaled_fmt(const void* A, int a_fmt, const float* sA, const void* B, int b_fmt,
-                                const float* sB, void* C, int64_t M, int64_t N, int64_t K, int out_dtype,
-                                hipStream_t stream) {
-  return gemm_impl(A, a_fmt, sA, B, b_fmt, sB, C, M, N, K, out_dtype, stream);
-}
-
-int dg_grouped_gemm_fp8_fmt(const void* A, int a_fmt, const float* sA, const void* B, int b_fmt,
-                            const float* sB, void* C, const int32_t* group_offsets, int num_groups,
-                            int64_t M_total, int64_t N, int64_t K, int out_dtype, hipStream_t stream) {
-  return grouped_impl(A, a_fmt, sA, B, b_fmt, sB, C, group_offsets, num_groups, M_total, N, K, out_dtype,
-                      stream);
 }
 
 int dg_quantize_fp8_blockscaled(const void* X, int in_dtype, void* Q, float* S, int64_t M, int64_t K,

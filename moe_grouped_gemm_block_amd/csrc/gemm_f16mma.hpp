@@ -152,6 +152,13 @@ __device__ __forceinline__ void copy16_to_lds(const i32x4& rsrc, uint32_t voff, 
                : "memory");
 }
 
+// 4 bytes per lane from buffer `rsrc` at byte offset `voff` into LDS at
+// `lds_base` + 4 * lane (same conventions as copy16_to_lds).
+__device__ __forceinline__ void copy4_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t lds_base) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_base)
+               : "memory");
+}
+
 struct GemmArgs {
   const uint8_t* A;       // [M][K]
   const float* sA;        // [ceil(M/128)][K/128]
@@ -187,7 +194,9 @@ __device__ __forceinline__ void tile_of(int bid, int m_tiles, int n_tiles, int& 
   tn = r / gsize;
 }
 
-template <int NWM, int NWN, bool OUT_BF16, int FA = FMT_E4M3, int FB = FMT_E4M3>
+// ROW_SA: sA holds one scale per row and K-block ([rows][K/128], the 1 x 128
+// per-token granularity) instead of one per 128 x 128 block.
+template <int NWM, int NWN, bool OUT_BF16, int FA = FMT_E4M3, int FB = FMT_E4M3, bool ROW_SA = false>
 __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   constexpr int WM = 64, WN = 128;             // wave sub-tile
   constexpr int MI = WM / 16, NI = WN / 16;    // 16x16 MFMA tiles per wave
@@ -197,8 +206,10 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   constexpr int A_CH = BM / 8 / NW, B_CH = BN / 8 / NW;   // 1 KB copy chunks per wave
   static_assert(A_CH * 8 * NW == BM && B_CH * 8 * NW == BN, "chunking");
   static_assert(NW % 2 == 0, "chunk parity per wave assumes an even wave count");
-  // LDS: [A stage 0][A stage 1][B stage 0][B stage 1]
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (A_BYTES + B_BYTES)];
+  constexpr int SA_BYTES = ROW_SA ? BM * 4 : 0;   // one K-block's row scales
+  static_assert(!ROW_SA || NW >= BM / 64, "row scales are copied by the first BM/64 waves");
+  // LDS: [A stage 0][A stage 1][B stage 0][B stage 1] ([sA stage 0][sA stage 1])
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (A_BYTES + B_BYTES + SA_BYTES)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -223,7 +234,7 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   // Scales are read through the constant address space so that they become
   // scalar loads (counted apart from the vector-memory copies into LDS).
   typedef const __attribute__((address_space(4))) float cfloat;
-  cfloat* sAr = (cfloat*)(p.sA + (size_t)mb * Kb);
+  cfloat* sAr = (cfloat*)(p.sA + (ROW_SA ? 0 : (size_t)mb * Kb));   // (unused with ROW_SA)
   cfloat* sBr = (cfloat*)(p.sB + ((size_t)e * Nb + nb) * Kb);
 
   // ---- global -> LDS copies --------------------------------------------------
@@ -246,7 +257,20 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   // LDS byte address of the buffer (wave-uniform)
   const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
       uint32_t(reinterpret_cast<uintptr_t>(static_cast<void*>(lds))));
+  // row scales of the tile: wave w < BM/64 copies rows 64 w .. 64 w + 63,
+  // 4 bytes per lane; rows past M read as zeros
+  i32x4 rS{};
+  uint32_t s_lane = 0;
+  if constexpr (ROW_SA) {
+    rS = make_rsrc(p.sA + (size_t)m0 * Kb, uint32_t(min(M - m0, BM)) * uint32_t(Kb) * 4u);
+    s_lane = uint32_t((wave * 64 + lane) * Kb * 4);
+  }
   auto issue_copies = [&](int kb, int stage) {
+    if constexpr (ROW_SA) {
+      if (wave < BM / 64)
+        copy4_to_lds(rS, s_lane + uint32_t(kb * 4),
+                     lds_addr + uint32_t(2 * (A_BYTES + B_BYTES) + stage * SA_BYTES + wave * 256));
+    }
     const uint32_t a_kb = opaque(a_lane + uint32_t(kb * KBLK));
     const uint32_t b_kb = opaque(b_lane + uint32_t(kb * KBLK));
 #pragma unroll
@@ -284,12 +308,20 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
     __syncthreads();
   }
 
-  float sa_next = Kb > 0 ? sAr[0] : 0.f, sb_next = Kb > 0 ? sBr[0] : 0.f;
+  float sa_next = Kb > 0 && !ROW_SA ? float(sAr[0]) : 1.f, sb_next = Kb > 0 ? sBr[0] : 0.f;
   for (int kb = 0; kb < Kb; ++kb) {
     const int stage = kb & 1;
     const float s = sa_next * sb_next;         // this K-block's fp32(sA * sB)
+    float s_m[MI];                              // the factor of row group mi
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) s_m[mi] = s;
+    if constexpr (ROW_SA) {
+      const float* ls = reinterpret_cast<const float*>(lds + 2 * (A_BYTES + B_BYTES) + stage * SA_BYTES);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) s_m[mi] = ls[wm + 16 * mi + r16] * sb_next;
+    }
     if (kb + 1 < Kb) {
-      sa_next = sAr[kb + 1];                   // prefetched one K-block ahead
+      if constexpr (!ROW_SA) sa_next = sAr[kb + 1];   // prefetched one K-block ahead
       sb_next = sBr[kb + 1];
       issue_copies(kb + 1, stage ^ 1);
     }
@@ -327,7 +359,7 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
           if (st == 0 && ni > 0) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              acc[mi][ni - 1][r] = __builtin_fmaf(s, part[mi][r], acc[mi][ni - 1][r]);
+              acc[mi][ni - 1][r] = __builtin_fmaf(s_m[mi], part[mi][r], acc[mi][ni - 1][r]);
           }
           part[mi] = mfma16_f16(bf[st], af[mi][st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : part[mi]);
         }
@@ -373,7 +405,7 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[mi][NI - 1][r] = __builtin_fmaf(s, part[mi][r], acc[mi][NI - 1][r]);
+      for (int r = 0; r < 4; ++r) acc[mi][NI - 1][r] = __builtin_fmaf(s_m[mi], part[mi][r], acc[mi][NI - 1][r]);
     wait_vmem();
     __syncthreads();
   }
@@ -420,18 +452,20 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
 // Named kernels (one per tile shape and output type) around the body.
 // One named kernel per tile shape, output type and pair of operand formats
 // (suffix _a<A format>b<B format>, 4 = E4M3, 5 = E5M2; E4M3 x E4M3 keeps the
-// plain name).
-#define DG_GEMM_KERNEL(NAME, NWM, NWN, BF16, FA, FB)                        \
+// plain name); suffix _rs: row-scaled A (1 x 128 scales).
+#define DG_GEMM_KERNEL(NAME, NWM, NWN, BF16, FA, FB, RS)                    \
   __global__ __launch_bounds__(64 * NWM * NWN, 1) void NAME(GemmArgs p) {   \
-    gemm_f16mma_body<NWM, NWN, BF16, FA, FB>(p);                            \
+    gemm_f16mma_body<NWM, NWN, BF16, FA, FB, RS>(p);                        \
   }
-#define DG_GEMM_SHAPE(SHAPE, NWM, NWN, SFX, FA, FB)                         \
-  DG_GEMM_KERNEL(dg_gemm_##SHAPE##_bf16##SFX, NWM, NWN, true, FA, FB)       \
-  DG_GEMM_KERNEL(dg_gemm_##SHAPE##_f32##SFX, NWM, NWN, false, FA, FB)
+#define DG_GEMM_SHAPE(SHAPE, NWM, NWN, SFX, FA, FB, RS)                     \
+  DG_GEMM_KERNEL(dg_gemm_##SHAPE##_bf16##SFX, NWM, NWN, true, FA, FB, RS)   \
+  DG_GEMM_KERNEL(dg_gemm_##SHAPE##_f32##SFX, NWM, NWN, false, FA, FB, RS)
 #define DG_GEMM_FORMATS(SFX, FA, FB)                                        \
-  DG_GEMM_SHAPE(128x512, 2, 4, SFX, FA, FB)                                 \
-  DG_GEMM_SHAPE(128x256, 2, 2, SFX, FA, FB)                                 \
-  DG_GEMM_SHAPE(128x128, 2, 1, SFX, FA, FB)
+  DG_GEMM_SHAPE(128x512, 2, 4, SFX, FA, FB, false)                          \
+  DG_GEMM_SHAPE(128x256, 2, 2, SFX, FA, FB, false)                          \
+  DG_GEMM_SHAPE(128x128, 2, 1, SFX, FA, FB, false)                          \
+  DG_GEMM_SHAPE(128x256, 2, 2, SFX##_rs, FA, FB, true)                      \
+  DG_GEMM_SHAPE(128x128, 2, 1, SFX##_rs, FA, FB, true)
 DG_GEMM_FORMATS(, FMT_E4M3, FMT_E4M3)
 DG_GEMM_FORMATS(_a5b5, FMT_E5M2, FMT_E5M2)
 DG_GEMM_FORMATS(_a4b5, FMT_E4M3, FMT_E5M2)

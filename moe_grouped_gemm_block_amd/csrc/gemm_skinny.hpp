@@ -23,16 +23,19 @@
 
 namespace dg {
 
-template <int MI, int NI, bool OUT_BF16, int FA = FMT_E4M3, int FB = FMT_E4M3>
+// ROW_SA: sA holds one scale per row and K-block ([M][K/128]).
+template <int MI, int NI, bool OUT_BF16, int FA = FMT_E4M3, int FB = FMT_E4M3, bool ROW_SA = false>
 __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p) {
   constexpr int NW = 4;                         // waves, each a quarter of the K-blocks
   constexpr int RM = 16 * MI, CN = 16 * NI;     // rows / columns of the workgroup tile
   constexpr int A_BYTES = RM * KBLK, B_BYTES = CN * KBLK;
-  constexpr int WAVE_LDS = 2 * A_BYTES + 3 * B_BYTES;   // A: 2 stages, B: 3 stages
+  constexpr int S_BYTES = ROW_SA ? 256 : 0;     // 64 row scales of one K-block
+  constexpr int WAVE_LDS = 2 * A_BYTES + 3 * B_BYTES + 2 * S_BYTES;   // A: 2 stages, B: 3, sA: 2
   constexpr int A_CH = RM / 8, B_CH = CN / 8;   // 1 KB copy chunks per K-block
+  constexpr int A_OPS = A_CH + (ROW_SA ? 1 : 0); // A copy instructions per K-block (+ its row scales)
   constexpr int RED = NW * RM * CN * 4;         // partial sums for the reduction
   constexpr int LDS_BYTES = (NW * WAVE_LDS > RED) ? NW * WAVE_LDS : RED;
-  static_assert(2 * B_CH + A_CH < 64, "vmcnt range");
+  static_assert(2 * B_CH + A_OPS < 64, "vmcnt range");
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
 
   const int lane = threadIdx.x & 63;
@@ -58,7 +61,13 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p) {
   const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(
       uint32_t(reinterpret_cast<uintptr_t>(static_cast<void*>(lds))) + uint32_t(wave * WAVE_LDS));
 
-  // wave LDS: [A stage 0][A stage 1][B stage 0][B stage 1][B stage 2]
+  // row scales (ROW_SA): lane L copies sA[L][kb] (rows past M read as zeros)
+  i32x4 rS{};
+  if constexpr (ROW_SA) rS = make_rsrc(p.sA, uint32_t(M) * uint32_t(Kb) * 4u);
+  const uint32_t s_lane = uint32_t(lane * Kb * 4);
+  constexpr int S_OFF = 2 * A_BYTES + 3 * B_BYTES;   // wave LDS offset of the scale stages
+
+  // wave LDS: [A stage 0][A stage 1][B stage 0][B stage 1][B stage 2] ([sA stage 0][sA stage 1])
   auto issue_a = [&](int kb, int stage) {
     const uint32_t ev = opaque(lane_even + uint32_t(kb * KBLK));
     const uint32_t od = opaque(lane_odd + uint32_t(kb * KBLK));
@@ -66,6 +75,8 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p) {
 #pragma unroll
     for (int c = 0; c < A_CH; ++c)
       copy16_to_lds(rA, ((c & 1) ? od : ev) + uint32_t(8 * c * K), base + uint32_t(c * 1024));
+    if constexpr (ROW_SA)
+      copy4_to_lds(rS, s_lane + uint32_t(kb * 4), lds_wave + uint32_t(S_OFF + stage * S_BYTES));
   };
   auto issue_b = [&](int kb, int stage) {
     const uint32_t ev = opaque(lane_even + uint32_t(kb * KBLK));
@@ -98,20 +109,28 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p) {
   }
   for (int kb = wave; kb < Kb; kb += NW, ++j) {
     const int astage = j & 1;
-    float sa = sAr[kb];
+    const float sa = ROW_SA ? 1.f : float(sAr[kb]);
     float sb[NI];
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) sb[ni] = ((cfloat*)p.sB)[(size_t)nbk[ni] * Kb + kb];
     if (kb + 2 * NW < Kb) {
       issue_a(kb + NW, astage ^ 1);
       issue_b(kb + 2 * NW, bstage == 0 ? 2 : bstage - 1);
-      wait_vmem_n<2 * B_CH + A_CH>();
+      wait_vmem_n<2 * B_CH + A_OPS>();
     } else {
       if (kb + NW < Kb) issue_a(kb + NW, astage ^ 1);
       wait_vmem_n<0>();
     }
     const uint8_t* la = lw + astage * A_BYTES;
     const uint8_t* lb = lw + 2 * A_BYTES + bstage * B_BYTES;
+    float sa_m[MI];                               // A scale of row group mi
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) sa_m[mi] = sa;
+    if constexpr (ROW_SA) {
+      const float* ls = reinterpret_cast<const float*>(lw + S_OFF + astage * S_BYTES);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) sa_m[mi] = ls[16 * mi + r16];
+    }
     bstage = bstage == 2 ? 0 : bstage + 1;
     v8h af[MI][4];
 #pragma unroll
@@ -126,7 +145,6 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p) {
       const int4 y1 = *reinterpret_cast<const int4*>(lb + off1 + ni * 16 * KBLK);
       v8h bf[4];
       fp8x32_to_f16<FB>(y0, y1, bf);
-      const float s = sa * sb[ni];
       v4f part[MI];
 #pragma unroll
       for (int st = 0; st < 4; ++st)
@@ -134,9 +152,11 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p) {
         for (int mi = 0; mi < MI; ++mi)
           part[mi] = mfma16_f16(bf[st], af[mi][st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : part[mi]);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+      for (int mi = 0; mi < MI; ++mi) {
+        const float s = sa_m[mi] * sb[ni];      // fp32(sA * sB) of this row group and K-block
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[mi][ni][r] = __builtin_fmaf(s, part[mi][r], acc[mi][ni][r]);
+      }
     }
   }
 
@@ -183,20 +203,24 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p) {
   }
 }
 
-#define DG_SKINNY_KERNEL(NAME, MI, NI, BF16, FA, FB) \
-  __global__ __launch_bounds__(256, 1) void NAME(GemmArgs p) { gemm_skinny_body<MI, NI, BF16, FA, FB>(p); }
-#define DG_SKINNY_SHAPE(ROWS, COLS, MI, NI, SFX, FA, FB)                                \
-  DG_SKINNY_KERNEL(dg_skinny_m##ROWS##_n##COLS##_bf16##SFX, MI, NI, true, FA, FB)       \
-  DG_SKINNY_KERNEL(dg_skinny_m##ROWS##_n##COLS##_f32##SFX, MI, NI, false, FA, FB)
-#define DG_SKINNY_FORMATS(SFX, FA, FB)                                                  \
-  DG_SKINNY_SHAPE(64, 48, 4, 3, SFX, FA, FB) DG_SKINNY_SHAPE(64, 16, 4, 1, SFX, FA, FB) \
-  DG_SKINNY_SHAPE(32, 48, 2, 3, SFX, FA, FB) DG_SKINNY_SHAPE(32, 16, 2, 1, SFX, FA, FB) \
-  DG_SKINNY_SHAPE(16, 48, 1, 3, SFX, FA, FB) DG_SKINNY_SHAPE(16, 16, 1, 1, SFX, FA, FB)
+#define DG_SKINNY_KERNEL(NAME, MI, NI, BF16, FA, FB, RS) \
+  __global__ __launch_bounds__(256, 1) void NAME(GemmArgs p) { gemm_skinny_body<MI, NI, BF16, FA, FB, RS>(p); }
+#define DG_SKINNY_SHAPE(ROWS, COLS, MI, NI, SFX, FA, FB, RS)                                \
+  DG_SKINNY_KERNEL(dg_skinny_m##ROWS##_n##COLS##_bf16##SFX, MI, NI, true, FA, FB, RS)       \
+  DG_SKINNY_KERNEL(dg_skinny_m##ROWS##_n##COLS##_f32##SFX, MI, NI, false, FA, FB, RS)
+#define DG_SKINNY_ROWS(SFX, FA, FB, RS)                                                     \
+  DG_SKINNY_SHAPE(64, 48, 4, 3, SFX, FA, FB, RS) DG_SKINNY_SHAPE(64, 16, 4, 1, SFX, FA, FB, RS) \
+  DG_SKINNY_SHAPE(32, 48, 2, 3, SFX, FA, FB, RS) DG_SKINNY_SHAPE(32, 16, 2, 1, SFX, FA, FB, RS) \
+  DG_SKINNY_SHAPE(16, 48, 1, 3, SFX, FA, FB, RS) DG_SKINNY_SHAPE(16, 16, 1, 1, SFX, FA, FB, RS)
+#define DG_SKINNY_FORMATS(SFX, FA, FB)   \
+  DG_SKINNY_ROWS(SFX, FA, FB, false)     \
+  DG_SKINNY_ROWS(SFX##_rs, FA, FB, true)
 DG_SKINNY_FORMATS(, FMT_E4M3, FMT_E4M3)
 DG_SKINNY_FORMATS(_a5b5, FMT_E5M2, FMT_E5M2)
 DG_SKINNY_FORMATS(_a4b5, FMT_E4M3, FMT_E5M2)
 DG_SKINNY_FORMATS(_a5b4, FMT_E5M2, FMT_E4M3)
 #undef DG_SKINNY_FORMATS
+#undef DG_SKINNY_ROWS
 #undef DG_SKINNY_SHAPE
 #undef DG_SKINNY_KERNEL
 

@@ -28,8 +28,8 @@ DG_ERR_INVALID_ARG = -1
 DG_ERR_UNSUPPORTED = -2
 DG_ERR_LAUNCH = -3
 
-EXPORTED = ("dg_gemm_fp8_blockscaled", "dg_grouped_gemm_fp8", "dg_gemm_fp8_blockscaled_fmt",
-            "dg_grouped_gemm_fp8_fmt", "dg_quantize_fp8_blockscaled", "dg_status_string")
+EXPORTED = ("dg_gemm_fp8_blockscaled", "dg_grouped_gemm_fp8", "dg_gemm_fp8_ex",
+            "dg_grouped_gemm_fp8_ex", "dg_quantize_fp8_blockscaled", "dg_status_string")
 
 _lib = None
 
@@ -48,10 +48,10 @@ def lib() -> ctypes.CDLL:
         L.dg_gemm_fp8_blockscaled.restype = ci
         L.dg_grouped_gemm_fp8.argtypes = [vp, vp, vp, vp, vp, vp, ci, i64, i64, i64, ci, vp]
         L.dg_grouped_gemm_fp8.restype = ci
-        L.dg_gemm_fp8_blockscaled_fmt.argtypes = [vp, ci, vp, vp, ci, vp, vp, i64, i64, i64, ci, vp]
-        L.dg_gemm_fp8_blockscaled_fmt.restype = ci
-        L.dg_grouped_gemm_fp8_fmt.argtypes = [vp, ci, vp, vp, ci, vp, vp, vp, ci, i64, i64, i64, ci, vp]
-        L.dg_grouped_gemm_fp8_fmt.restype = ci
+        L.dg_gemm_fp8_ex.argtypes = [vp, ci, vp, ci, vp, ci, vp, vp, i64, i64, i64, ci, vp]
+        L.dg_gemm_fp8_ex.restype = ci
+        L.dg_grouped_gemm_fp8_ex.argtypes = [vp, ci, vp, ci, vp, ci, vp, vp, vp, ci, i64, i64, i64, ci, vp]
+        L.dg_grouped_gemm_fp8_ex.restype = ci
         L.dg_quantize_fp8_blockscaled.argtypes = [vp, ci, vp, vp, i64, i64, ci, vp]
         L.dg_quantize_fp8_blockscaled.restype = ci
         L.dg_status_string.argtypes = [ci]
@@ -72,14 +72,14 @@ def dg_grouped_gemm_fp8(A, sA, B, sB, C, group_offsets, num_groups, M_total, N, 
                                      N, K, out_dtype, stream)
 
 
-def dg_gemm_fp8_blockscaled_fmt(A, a_fmt, sA, B, b_fmt, sB, C, M, N, K, out_dtype, stream) -> int:
-    return lib().dg_gemm_fp8_blockscaled_fmt(A, a_fmt, sA, B, b_fmt, sB, C, M, N, K, out_dtype, stream)
+def dg_gemm_fp8_ex(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, M, N, K, out_dtype, stream) -> int:
+    return lib().dg_gemm_fp8_ex(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, M, N, K, out_dtype, stream)
 
 
-def dg_grouped_gemm_fp8_fmt(A, a_fmt, sA, B, b_fmt, sB, C, group_offsets, num_groups, M_total, N, K,
-                            out_dtype, stream) -> int:
-    return lib().dg_grouped_gemm_fp8_fmt(A, a_fmt, sA, B, b_fmt, sB, C, group_offsets, num_groups,
-                                         M_total, N, K, out_dtype, stream)
+def dg_grouped_gemm_fp8_ex(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, group_offsets, num_groups, M_total,
+                           N, K, out_dtype, stream) -> int:
+    return lib().dg_grouped_gemm_fp8_ex(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, group_offsets, num_groups,
+                                        M_total, N, K, out_dtype, stream)
 
 
 def dg_quantize_fp8_blockscaled(X, in_dtype, Q, S, M, K, block_rows, stream) -> int:
@@ -151,26 +151,40 @@ def _stream(stream):
     return getattr(stream, "cuda_stream", stream)
 
 
+def _sa_rows(sA, M, K):
+    """Rows per A scale block implied by sA's shape: 128 ([ceil(M/128)][K/128])
+    or 1 ([M][K/128]); the first wins where both fit (M <= 1)."""
+    if tuple(sA.shape) == (-(-M // 128), K // 128):
+        return 128
+    if tuple(sA.shape) == (M, K // 128):
+        return 1
+    raise ValueError(f"sA has shape {tuple(sA.shape)}; expected {(-(-M // 128), K // 128)} "
+                     f"(128 x 128 blocks) or {(M, K // 128)} (1 x 128 blocks)")
+
+
 def gemm_fp8_blockscaled(A, sA, B, sB, out_dtype="bf16", C=None, stream=None, a_fmt="e4m3", b_fmt="e4m3"):
     """C[M][N] = block-scaled A[M][K] x B (stored [N][K]) on the device; the
-    operands' FP8 formats are "e4m3" (default) or "e5m2"."""
+    operands' FP8 formats are "e4m3" (default) or "e5m2".  sA holds one scale
+    per 128 x 128 block ([ceil(M/128)][K/128]) or per row and 128 columns
+    ([M][K/128])."""
     _check_fp8(A, "A")
     _check_fp8(B, "B")
     M, K = A.shape
     N, K2 = B.shape
     if K != K2:
         raise ValueError("A and B must share K")
-    _check_f32(sA, "sA", (-(-M // 128), K // 128))
+    rows = _sa_rows(sA, M, K)
+    _check_f32(sA, "sA", tuple(sA.shape))
     _check_f32(sB, "sB", (-(-N // 128), K // 128))
     code = out_code(out_dtype)
     C = _out(C, M, N, code, A)
     fa, fb = fmt_code(a_fmt), fmt_code(b_fmt)
-    if fa == DG_FP8_E4M3 and fb == DG_FP8_E4M3:
+    if fa == DG_FP8_E4M3 and fb == DG_FP8_E4M3 and rows == 128:
         st = dg_gemm_fp8_blockscaled(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(),
                                      C.data_ptr(), M, N, K, code, _stream(stream))
     else:
-        st = dg_gemm_fp8_blockscaled_fmt(A.data_ptr(), fa, sA.data_ptr(), B.data_ptr(), fb, sB.data_ptr(),
-                                         C.data_ptr(), M, N, K, code, _stream(stream))
+        st = dg_gemm_fp8_ex(A.data_ptr(), fa, sA.data_ptr(), rows, B.data_ptr(), fb, sB.data_ptr(),
+                            C.data_ptr(), M, N, K, code, _stream(stream))
     if st != DG_OK:
         raise DGError(st, "dg_gemm_fp8_blockscaled")
     return C
@@ -186,7 +200,8 @@ def grouped_gemm_fp8(A, sA, B, sB, group_offsets, out_dtype="bf16", C=None, stre
     G, N, K2 = B.shape
     if K != K2:
         raise ValueError("A and B must share K")
-    _check_f32(sA, "sA", (M_total // 128, K // 128))
+    rows = _sa_rows(sA, M_total, K)
+    _check_f32(sA, "sA", tuple(sA.shape))
     _check_f32(sB, "sB", (G, -(-N // 128), K // 128))
     if (group_offsets.dtype != torch.int32 or not group_offsets.is_cuda
             or tuple(group_offsets.shape) != (G + 1,)):
@@ -194,14 +209,14 @@ def grouped_gemm_fp8(A, sA, B, sB, group_offsets, out_dtype="bf16", C=None, stre
     code = out_code(out_dtype)
     C = _out(C, M_total, N, code, A)
     fa, fb = fmt_code(a_fmt), fmt_code(b_fmt)
-    if fa == DG_FP8_E4M3 and fb == DG_FP8_E4M3:
+    if fa == DG_FP8_E4M3 and fb == DG_FP8_E4M3 and rows == 128:
         st = dg_grouped_gemm_fp8(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(),
                                  C.data_ptr(), group_offsets.data_ptr(), G, M_total, N, K, code,
                                  _stream(stream))
     else:
-        st = dg_grouped_gemm_fp8_fmt(A.data_ptr(), fa, sA.data_ptr(), B.data_ptr(), fb, sB.data_ptr(),
-                                     C.data_ptr(), group_offsets.data_ptr(), G, M_total, N, K, code,
-                                     _stream(stream))
+        st = dg_grouped_gemm_fp8_ex(A.data_ptr(), fa, sA.data_ptr(), rows, B.data_ptr(), fb, sB.data_ptr(),
+                                    C.data_ptr(), group_offsets.data_ptr(), G, M_total, N, K, code,
+                                    _stream(stream))
     if st != DG_OK:
         raise DGError(st, "dg_grouped_gemm_fp8")
     return C

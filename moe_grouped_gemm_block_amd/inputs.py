@@ -104,38 +104,41 @@ def encode_e5m2(v: np.ndarray) -> np.ndarray:
 ENCODERS = {"e4m3": encode_e4m3, "e5m2": encode_e5m2}
 
 
-def block_scales(x: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
-    """Per-128x128-block scale fp32(amax/fmax) of a float32 [R][K] matrix
-    (fmax = 448 for E4M3, 57344 for E5M2).
+def block_scales(x: np.ndarray, fmt: str = "e4m3", rows: int = BLOCK) -> np.ndarray:
+    """Per-block scale fp32(amax/fmax) of a float32 [R][K] matrix (fmax = 448
+    for E4M3, 57344 for E5M2), blocks of `rows` (128 or 1) x 128.
 
-    Returns float32 [ceil(R/128)][K/128]; all-zero blocks get 1.0.  The last
-    row block may be partial (R not a multiple of 128).
+    Returns float32 [ceil(R/rows)][K/128]; all-zero blocks get 1.0.  The last
+    row block may be partial (R not a multiple of rows).
     """
     R, K = x.shape
     assert K % BLOCK == 0, "K must be a multiple of 128"
-    Rb, Kb = -(-R // BLOCK), K // BLOCK
-    pad = Rb * BLOCK - R
+    assert rows in (1, BLOCK)
+    Rb, Kb = -(-R // rows), K // BLOCK
+    pad = Rb * rows - R
     xa = np.abs(x)
     if pad:
         xa = np.concatenate([xa, np.zeros((pad, K), np.float32)], axis=0)
-    amax = xa.reshape(Rb, BLOCK, Kb, BLOCK).max(axis=(1, 3)).astype(np.float32)
+    amax = xa.reshape(Rb, rows, Kb, BLOCK).max(axis=(1, 3)).astype(np.float32)
     s = amax / np.float32(FMT_MAX[fmt])       # fp32 division, RNE
     s = np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
     return s
 
 
-def quantize(x: np.ndarray, row_chunk: int = 1024, fmt: str = "e4m3") -> tuple[np.ndarray, np.ndarray]:
-    """Quantise float32 [R][K] -> (codes uint8 [R][K], scales fp32 [Rb][Kb])."""
+def quantize(x: np.ndarray, row_chunk: int = 1024, fmt: str = "e4m3",
+             rows: int = BLOCK) -> tuple[np.ndarray, np.ndarray]:
+    """Quantise float32 [R][K] -> (codes uint8 [R][K], scales fp32 [ceil(R/rows)][K/128])
+    with `rows` x 128 scale blocks (rows = 128 or 1)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     R, K = x.shape
-    s = block_scales(x, fmt)
+    s = block_scales(x, fmt, rows)
     enc = ENCODERS[fmt]
     q = np.empty((R, K), np.uint8)
     s64 = s.astype(np.float64)
     for r0 in range(0, R, row_chunk):           # bounded temporaries
         r1 = min(R, r0 + row_chunk)
-        rows = np.arange(r0, r1) // BLOCK
-        sexp = np.repeat(s64[rows], BLOCK, axis=1)          # [rows][K]
+        srow = np.arange(r0, r1) // rows
+        sexp = np.repeat(s64[srow], BLOCK, axis=1)          # [rows][K]
         q[r0:r1] = enc(x[r0:r1].astype(np.float64) / sexp)
     return q, s
 
@@ -148,7 +151,7 @@ def quantize(x: np.ndarray, row_chunk: int = 1024, fmt: str = "e4m3") -> tuple[n
 class Problem:
     """One GEMM workload: E4M3 codes, FP32 block scales and metadata.
 
-    Dense: A [M][K], sA [ceil(M/128)][K/128], B [N][K], sB [ceil(N/128)][K/128].
+    Dense: A [M][K], sA [ceil(M/sa_rows)][K/128], B [N][K], sB [ceil(N/128)][K/128].
     Grouped: A [M_total][K], B [G][N][K], sB [G][ceil(N/128)][K/128] and
     group_offsets int32 [G+1] (multiples of 128, o_0 = 0, o_G = M_total).
     """
@@ -166,6 +169,7 @@ class Problem:
     real_rows: int | None = None        # rows that carry tokens (grouped)
     a_fmt: str = "e4m3"                 # code format of A / B: "e4m3" or "e5m2"
     b_fmt: str = "e4m3"
+    sa_rows: int = BLOCK                # rows per A scale block: 128 or 1 (per token)
 
     @property
     def grouped(self) -> bool:
@@ -199,10 +203,10 @@ def dense_problem(M: int, N: int, K: int, seed: int, out_dtype: str = "bf16",
                   a_std: float = 1.0, b_std: float = 1.0,
                   block_log2_range: float = 0.0, outlier_frac: float = 0.0,
                   outlier_mult: float = 50.0, name: str = "dense",
-                  a_fmt: str = "e4m3", b_fmt: str = "e4m3") -> Problem:
+                  a_fmt: str = "e4m3", b_fmt: str = "e4m3", sa_rows: int = BLOCK) -> Problem:
     """Gaussian A [M][K] and B [N][K] with optional per-block multipliers and
     per-element outliers, quantised to E4M3 (or E5M2) with 128x128 block
-    scales."""
+    scales (A: sa_rows x 128 blocks)."""
     r_act, r_w, r_mod, _ = streams(seed)
     A = r_act.standard_normal((M, K), dtype=np.float32) * np.float32(a_std)
     B = r_w.standard_normal((N, K), dtype=np.float32) * np.float32(b_std)
@@ -217,10 +221,10 @@ def dense_problem(M: int, N: int, K: int, seed: int, out_dtype: str = "bf16",
     if outlier_frac:
         hit = r_mod.random((M, K)) < outlier_frac
         A[hit] *= np.float32(outlier_mult)
-    qA, sA = quantize(A, fmt=a_fmt)
+    qA, sA = quantize(A, fmt=a_fmt, rows=sa_rows)
     qB, sB = quantize(B, fmt=b_fmt)
     return Problem(name=name, A=qA, sA=sA, B=qB, sB=sB, M=M, N=N, K=K,
-                   out_dtype=out_dtype, seed=seed, a_fmt=a_fmt, b_fmt=b_fmt)
+                   out_dtype=out_dtype, seed=seed, a_fmt=a_fmt, b_fmt=b_fmt, sa_rows=sa_rows)
 
 
 def route_top2(rng: np.random.Generator, T: int, weights: np.ndarray) -> np.ndarray:
@@ -238,7 +242,7 @@ def route_top2(rng: np.random.Generator, T: int, weights: np.ndarray) -> np.ndar
 def grouped_problem(G: int, N: int, K: int, T: int, seed: int,
                     popularity: str = "uniform", zipf_s: float = 1.1,
                     zero_lowest: int = 4, b_std: float = 0.02,
-                    out_dtype: str = "bf16", name: str = "grouped") -> Problem:
+                    out_dtype: str = "bf16", name: str = "grouped", sa_rows: int = BLOCK) -> Problem:
     """MoE expert GEMM over the contiguous padded layout.
 
     Token activations X [T][K] ~ N(0,1); expert weights B_e [N][K] ~ N(0,b_std);
@@ -258,11 +262,11 @@ def grouped_problem(G: int, N: int, K: int, T: int, seed: int,
     A = np.zeros((M_total, K), np.float32)
     for e in range(G):
         A[offsets[e]:offsets[e] + counts[e]] = X[seg_tokens[e]]
-    qA, sA = quantize(A)
+    qA, sA = quantize(A, rows=sa_rows)
     return Problem(name=name, A=qA, sA=sA, B=Bq, sB=sB, M=M_total, N=N, K=K,
                    out_dtype=out_dtype, seed=seed,
                    group_offsets=offsets.astype(np.int32),
-                   real_rows=int(counts.sum()))
+                   real_rows=int(counts.sum()), sa_rows=sa_rows)
 
 
 def route(G: int, T: int, rng: np.random.Generator, popularity: str = "uniform",
@@ -308,28 +312,28 @@ CONFIG_NAMES = {
 }
 
 
-def make_config(i: int, seed: int | None = None, fmt: str = "e4m3") -> Problem:
+def make_config(i: int, seed: int | None = None, fmt: str = "e4m3", sa_rows: int = BLOCK) -> Problem:
     """Workload i (1..5); the default seed is the workload index.  fmt =
     "e5m2" quantises both operands of the dense workloads 1-3 to E5M2
-    instead (same data, name suffixed with _e5m2)."""
+    instead (same data, name suffixed with _e5m2).  sa_rows = 1 gives A one
+    scale per token and 128 columns (name suffixed with _a1x128)."""
     s = i if seed is None else seed
     if fmt != "e4m3" and i > 3:
         raise ValueError("E5M2 variants exist for the dense workloads 1-3")
-    sfx = "" if fmt == "e4m3" else f"_{fmt}"
+    sfx = ("" if fmt == "e4m3" else f"_{fmt}") + ("" if sa_rows == BLOCK else "_a1x128")
+    kw = dict(a_fmt=fmt, b_fmt=fmt, sa_rows=sa_rows)
     if i == 1:
-        return dense_problem(256, 256, 256, s, out_dtype="f32", name=CONFIG_NAMES[1] + sfx,
-                             a_fmt=fmt, b_fmt=fmt)
+        return dense_problem(256, 256, 256, s, out_dtype="f32", name=CONFIG_NAMES[1] + sfx, **kw)
     if i == 2:
         return dense_problem(4096, 4096, 4096, s, out_dtype="bf16",
-                             block_log2_range=4.0, name=CONFIG_NAMES[2] + sfx, a_fmt=fmt, b_fmt=fmt)
+                             block_log2_range=4.0, name=CONFIG_NAMES[2] + sfx, **kw)
     if i == 3:
         return dense_problem(64, 12288, 4096, s, out_dtype="bf16", b_std=0.02,
-                             outlier_frac=0.01, outlier_mult=50.0, name=CONFIG_NAMES[3] + sfx,
-                             a_fmt=fmt, b_fmt=fmt)
+                             outlier_frac=0.01, outlier_mult=50.0, name=CONFIG_NAMES[3] + sfx, **kw)
     if i == 4:
         return grouped_problem(8, 4096, 4096, 4096, s, popularity="uniform",
-                               name=CONFIG_NAMES[4])
+                               name=CONFIG_NAMES[4] + sfx, sa_rows=sa_rows)
     if i == 5:
         return grouped_problem(64, 2048, 2048, 8192, s, popularity="zipf",
-                               name=CONFIG_NAMES[5])
+                               name=CONFIG_NAMES[5] + sfx, sa_rows=sa_rows)
     raise ValueError(f"unknown workload {i}")

@@ -28,6 +28,10 @@ Sources:
     caller supplies both scale sets -- FP8-for-MoE page, section 4.3.
   * MoE grouped variant: every expert's rows sit in one contiguous matrix,
     one segment per expert -- nxmr.cn/news/132300, section 2.2.
+  * Per-row A scales (sa_rows = 1): the granularity table of the FP8 kernel
+    write-up (demingchina.com/news/60142, section 5.2) lists groups of 128
+    elements; for A that is one factor per row and 128-wide K-block, and the
+    definition above then reads sA[i, kb] in place of sA[i // 128, kb].
 
 Exactness: every E4M3 value is an integer multiple of 2^-9 below 2^9, so a
 product is a multiple of 2^-18 below 2^18 and a sum of up to 2^12 products
@@ -105,13 +109,18 @@ def decode(codes: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
 def gemm_blockscaled(A: np.ndarray, sA: np.ndarray, B: np.ndarray, sB: np.ndarray,
                      rows: np.ndarray | None = None,
                      cols: np.ndarray | None = None,
-                     a_fmt: str = "e4m3", b_fmt: str = "e4m3") -> tuple[np.ndarray, np.ndarray]:
+                     a_fmt: str = "e4m3", b_fmt: str = "e4m3",
+                     sa_rows: int = 128) -> tuple[np.ndarray, np.ndarray]:
     """Dense block-scaled GEMM.
 
-    A: uint8 [M][K] (row-major), sA: fp32 [ceil(M/128)][K/128]
+    A: uint8 [M][K] (row-major), sA: fp32 [ceil(M/sa_rows)][K/128]
     B: uint8 [N][K] (B column-major), sB: fp32 [ceil(N/128)][K/128]
     rows / cols: optional index subsets of the output to evaluate.
     a_fmt / b_fmt: "e4m3" (default) or "e5m2" codes.
+    sa_rows: rows of A per scale block: 128 (128 x 128 blocks) or 1 (one
+    scale per row and 128 columns, the 1 x 128 granularity of the FP8 kernel
+    write-up, demingchina.com/news/60142, section 5.2 table).  Row i of the
+    output then takes A scale sA[i // sa_rows, kb] for K-block kb.
 
     With an E5M2 operand a block partial can need more than 53 bits (E5M2
     values span 2^-16 .. 57344), so it is then exact only up to BLAS's
@@ -126,6 +135,8 @@ def gemm_blockscaled(A: np.ndarray, sA: np.ndarray, B: np.ndarray, sB: np.ndarra
     N, K2 = B.shape
     if K != K2 or K % BLOCK:
         raise ValueError("A and B must share K, a multiple of 128")
+    if sa_rows not in (1, BLOCK):
+        raise ValueError("sa_rows must be 1 or 128")
     Kb = K // BLOCK
     rows = np.arange(M) if rows is None else np.asarray(rows)
     cols = np.arange(N) if cols is None else np.asarray(cols)
@@ -139,7 +150,7 @@ def gemm_blockscaled(A: np.ndarray, sA: np.ndarray, B: np.ndarray, sB: np.ndarra
         b = B64[:, ks]
         partial = a @ b.T                                      # exact for E4M3 x E4M3
         absum = np.abs(a) @ np.abs(b).T                        # exact
-        scale = (sA[rows // BLOCK, kb].astype(np.float64)[:, None]
+        scale = (sA[rows // sa_rows, kb].astype(np.float64)[:, None]
                  * sB[cols // BLOCK, kb].astype(np.float64)[None, :])
         C += scale * partial
         mass += scale * absum
@@ -150,10 +161,11 @@ def grouped_gemm(A: np.ndarray, sA: np.ndarray, B: np.ndarray, sB: np.ndarray,
                  group_offsets: np.ndarray,
                  rows: np.ndarray | None = None,
                  cols: np.ndarray | None = None,
-                 a_fmt: str = "e4m3", b_fmt: str = "e4m3") -> tuple[np.ndarray, np.ndarray]:
+                 a_fmt: str = "e4m3", b_fmt: str = "e4m3",
+                 sa_rows: int = 128) -> tuple[np.ndarray, np.ndarray]:
     """MoE grouped block-scaled GEMM over contiguous expert segments.
 
-    A: uint8 [M_total][K]; sA: fp32 [M_total/128][K/128]
+    A: uint8 [M_total][K]; sA: fp32 [M_total/sa_rows][K/128] (sa_rows 128 or 1)
     B: uint8 [G][N][K];    sB: fp32 [G][ceil(N/128)][K/128]
     group_offsets: int [G+1], rows [o_e, o_{e+1}) belong to expert e.
     Each expert's rows are a dense product with that expert's B and sB.
@@ -174,12 +186,12 @@ def grouped_gemm(A: np.ndarray, sA: np.ndarray, B: np.ndarray, sB: np.ndarray,
         if len(sel) == 0:
             continue
         local = rows[sel] - lo
-        # the expert's A scale rows start at block lo/128
+        # the expert's A scale rows start at block lo / sa_rows
         if lo % BLOCK:
             raise ValueError("segment starts must be multiples of 128")
-        sA_e = sA[lo // BLOCK:(hi + BLOCK - 1) // BLOCK]
+        sA_e = sA[lo // sa_rows:(hi + sa_rows - 1) // sa_rows]
         Ce, me = gemm_blockscaled(A[lo:hi], sA_e, B[e], sB[e], rows=local, cols=cols,
-                                  a_fmt=a_fmt, b_fmt=b_fmt)
+                                  a_fmt=a_fmt, b_fmt=b_fmt, sa_rows=sa_rows)
         C[sel] = Ce
         mass[sel] = me
     return C, mass

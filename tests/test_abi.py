@@ -40,7 +40,7 @@ def L():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() >= {"dg_gemm_fp8_blockscaled", "dg_grouped_gemm_fp8",
-                                    "dg_gemm_fp8_blockscaled_fmt", "dg_grouped_gemm_fp8_fmt",
+                                    "dg_gemm_fp8_ex", "dg_grouped_gemm_fp8_ex",
                                     "dg_quantize_fp8_blockscaled", "dg_status_string"}
 
 
@@ -93,30 +93,39 @@ def test_grouped_validation(L, kw, want):
     assert grouped(**kw) == want
 
 
-def dense_fmt(fa=1, fb=1, **kw):
+def dense_ex(fa=1, fb=1, rows=128, **kw):
     d = dict(A=P, sA=P, B=P, sB=P, C=P, M=256, N=256, K=256, out=1)
     d.update(kw)
-    return dg.dg_gemm_fp8_blockscaled_fmt(d["A"], fa, d["sA"], d["B"], fb, d["sB"], d["C"], d["M"], d["N"],
-                                          d["K"], d["out"], None)
+    return dg.dg_gemm_fp8_ex(d["A"], fa, d["sA"], rows, d["B"], fb, d["sB"], d["C"], d["M"], d["N"],
+                             d["K"], d["out"], None)
 
 
-def grouped_fmt(fa=1, fb=0, **kw):
+def grouped_ex(fa=1, fb=0, rows=128, **kw):
     d = dict(A=P, sA=P, B=P, sB=P, C=P, offs=P, G=4, M=512, N=256, K=256, out=1)
     d.update(kw)
-    return dg.dg_grouped_gemm_fp8_fmt(d["A"], fa, d["sA"], d["B"], fb, d["sB"], d["C"], d["offs"], d["G"],
-                                      d["M"], d["N"], d["K"], d["out"], None)
+    return dg.dg_grouped_gemm_fp8_ex(d["A"], fa, d["sA"], rows, d["B"], fb, d["sB"], d["C"], d["offs"],
+                                     d["G"], d["M"], d["N"], d["K"], d["out"], None)
 
 
+@pytest.mark.parametrize("rows", [128, 1])
 @pytest.mark.parametrize("fa,fb,kw,want", [
     (2, 0, {}, INVALID), (0, -1, {}, INVALID), (1, 1, dict(A=None), INVALID), (1, 0, dict(K=200), UNSUP),
     (0, 1, dict(out=3), INVALID), (1, 1, dict(M=0), OK), (0, 1, dict(N=12), UNSUP),
+    (0, 0, dict(sA=P + 2), INVALID), (0, 0, dict(sA=None), INVALID),
 ])
-def test_format_entry_points_validation(L, fa, fb, kw, want):
-    assert dense_fmt(fa, fb, **kw) == want
+def test_general_entry_points_validation(L, fa, fb, rows, kw, want):
+    assert dense_ex(fa, fb, rows, **kw) == want
     gkw = {k: v for k, v in kw.items() if k != "M"}
     if "M" not in kw:
-        assert grouped_fmt(fa, fb, **gkw) == want
-    assert grouped_fmt(1, 1, G=0) == INVALID and grouped_fmt(7, 1) == INVALID
+        assert grouped_ex(fa, fb, rows, **gkw) == want
+    assert grouped_ex(1, 1, rows, G=0) == INVALID and grouped_ex(7, 1, rows) == INVALID
+
+
+@pytest.mark.parametrize("rows", [0, 2, 64, 127, 129, -1])
+def test_general_entry_points_reject_scale_granularity(L, rows):
+    assert dense_ex(0, 0, rows) == INVALID
+    assert grouped_ex(0, 0, rows) == INVALID
+    assert dense_ex(0, 0, rows, M=0) == INVALID        # checked before the empty-work shortcut
 
 
 def quant(X=P, dt=1, Q=P, S=P, M=256, K=256, R=128):
