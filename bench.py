@@ -23,6 +23,8 @@ Workloads (seeded, synthetic; see inputs.make_config):
   3  skinny 64 x 12288 x 4096, outliers, BF16   (HBM-bound)
   4  MoE 8 experts, N = K = 4096, top-2 uniform
   5  MoE 64 experts, N = K = 2048, top-2 Zipf(1.1)
+  6  one decode step of workload 5's MoE: 128 tokens, packed segments,
+     per-token A scales                        (HBM-bound)
 
 --op quantize times the activation quantisation that produces A instead
 (4096 x 4096 BF16 in, E4M3 codes and FP32 block scales out; HBM-bound).
@@ -44,7 +46,8 @@ METRIC = "FP8 block-scaled GEMM TFLOPS (% of FP8 MFMA peak); HBM GB/s for M≤64
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA (no sparsity)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 INFINITY_CACHE = 256 << 20
-HBM_BOUND = {3, 5}           # workloads whose roofline is HBM bandwidth
+HBM_BOUND = {3, 5, 6}        # workloads whose roofline is HBM bandwidth
+GBS_VALUE = {3, 6}           # workloads whose `value` is GB/s (streaming B once)
 QUANT_METRIC = "FP8 activation quantisation HBM GB/s (BF16 in, E4M3 + FP32 block scales out)"
 
 
@@ -142,6 +145,60 @@ def cpu_baseline_quant(x, block_rows: int, target_s: float = 10.0):
                       "one thread (per-block Python loop)"}
 
 
+def run_timed(step, K: int, W: int, use_graph: bool):
+    """W untimed warm-up steps, then exactly K timed steps between
+    torch.cuda.synchronize() calls.  step(i, stream_handle) enqueues step i.
+
+    With use_graph the K timed steps are captured once into a HIP graph and
+    the timed region is one replay of it: kernels of a few microseconds are
+    otherwise paced by the host's launch rate rather than by the GPU (the
+    graph is replayed once, untimed, before the timed replay).  Returns
+    (wall ms per step, kernel ms per step from HIP events on the launch
+    stream, per-step event times or None)."""
+    import numpy as np
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(W):
+        step(i, stream.cuda_stream)
+    torch.cuda.synchronize()
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+            h = torch.cuda.current_stream().cuda_stream
+            for i in range(K):
+                step(W + i, h)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        t_start = time.perf_counter()
+        ev[0].record(stream)
+        g.replay()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        t_end = time.perf_counter()
+        per = None
+        kern_ms = float(ev[0].elapsed_time(ev[1])) / K
+    else:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        t_start = time.perf_counter()
+        for i in range(K):
+            ev[i].record(stream)
+            step(W + i, stream.cuda_stream)
+        ev[K].record(stream)
+        torch.cuda.synchronize()
+        t_end = time.perf_counter()
+        per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(K)])
+        kern_ms = float(ev[0].elapsed_time(ev[K])) / K
+    ms_step = (t_end - t_start) * 1e3 / K
+    if per is None:
+        log(f"kernel ms (HIP events, graph of {K} steps): mean {kern_ms:.4f}; wall ms/step {ms_step:.4f}")
+    else:
+        log(f"kernel ms (HIP events): mean {kern_ms:.4f}  p10 {np.percentile(per, 10):.4f}  "
+            f"p50 {np.percentile(per, 50):.4f}  p90 {np.percentile(per, 90):.4f}; wall ms/step {ms_step:.4f}")
+    return ms_step, kern_ms, per
+
+
 def bench_quantize(args):
     import numpy as np
     import torch
@@ -165,33 +222,16 @@ def bench_quantize(args):
         Q = torch.empty((M, K), dtype=torch.uint8, device=dev)
         S = torch.empty((-(-M // R_blk), K // 128), dtype=torch.float32, device=dev)
         copies.append((X, Q, S))
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
+    ptrs = [(X.data_ptr(), Q.data_ptr(), S.data_ptr()) for X, Q, S in copies]
 
-    def step(i):
-        X, Q, S = copies[i % R]
-        st = dg.dg_quantize_fp8_blockscaled(X.data_ptr(), dg.DG_IN_BF16, Q.data_ptr(), S.data_ptr(),
-                                            M, K, R_blk, sh)
+    def step(i, sh):
+        x, q, s = ptrs[i % R]
+        st = dg.dg_quantize_fp8_blockscaled(x, dg.DG_IN_BF16, q, s, M, K, R_blk, sh)
         if st != dg.DG_OK:
             raise dg.DGError(st, "bench step")
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
     n = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
-    t_start = time.perf_counter()
-    for i in range(n):
-        ev[i].record(stream)
-        step(args.warmup + i)
-    ev[n].record(stream)
-    torch.cuda.synchronize()
-    t_end = time.perf_counter()
-    ms_step = (t_end - t_start) * 1e3 / n
-    kern_ms = float(ev[0].elapsed_time(ev[n])) / n
-    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
-    log(f"kernel ms (HIP events): mean {kern_ms:.4f}  p10 {np.percentile(per, 10):.4f}  "
-        f"p50 {np.percentile(per, 50):.4f}  p90 {np.percentile(per, 90):.4f}; wall ms/step {ms_step:.4f}")
+    ms_step, kern_ms, _ = run_timed(step, n, args.warmup, not args.no_graph)
     name = f"quantize_{M}x{K}_bf16_{R_blk}x128"
     achieved = step_bytes / (kern_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -201,7 +241,8 @@ def bench_quantize(args):
             "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16->e4m3",
             "data": "synthetic",
-            "config": {"workload": name, "M": M, "K": K, "block_rows": R_blk, "seed": 2, "operand_copies": R},
+            "config": {"workload": name, "M": M, "K": K, "block_rows": R_blk, "seed": 2, "operand_copies": R,
+                       "launch": "eager" if args.no_graph else "hip_graph"},
             "roofline": roof, "cpu_baseline": cpu, "kernel_ms": round(kern_ms, 5)}
     print(json.dumps(line), flush=True)
 
@@ -211,9 +252,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--rotate", type=int, default=0, help="operand copies (0 = enough to exceed the Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch the timed steps one by one from Python instead of replaying a HIP graph")
     ap.add_argument("--op", choices=["gemm", "quantize"], default="gemm")
     ap.add_argument("--a-scale", choices=["128x128", "1x128"], default="128x128",
                     help="A scale blocks of the GEMM: 128x128, or one per token and 128 columns")
@@ -275,56 +318,35 @@ def main():
         d["C"] = torch.empty((p.M, p.N), dtype=cdt, device=dev)
         copies.append(d)
     log(f"{R} operand copies resident ({R * step_bytes / 2**20:.0f} MiB)")
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
     code = dg.out_code(p.out_dtype)
+    ptrs = [{k: v.data_ptr() for k, v in d.items()} for d in copies]
+    plain = p.a_fmt == "e4m3" and p.b_fmt == "e4m3" and p.sa_rows == 128
+    fa, fb = dg.fmt_code(p.a_fmt), dg.fmt_code(p.b_fmt)
 
-    def step(i):
-        d = copies[i % R]
-        plain = p.a_fmt == "e4m3" and p.b_fmt == "e4m3" and p.sa_rows == 128
-        fa, fb = dg.fmt_code(p.a_fmt), dg.fmt_code(p.b_fmt)
-        if p.grouped and plain:
-            st = dg.dg_grouped_gemm_fp8(d["A"].data_ptr(), d["sA"].data_ptr(), d["B"].data_ptr(),
-                                        d["sB"].data_ptr(), d["C"].data_ptr(), d["offs"].data_ptr(),
+    def step(i, sh):
+        d = ptrs[i % R]
+        if p.packed:
+            st = dg.dg_grouped_gemm_fp8_segments(d["A"], fa, d["sA"], d["B"], fb, d["sB"], d["C"], d["offs"],
+                                                 p.G, p.M, p.N, p.K, code, sh)
+        elif p.grouped and plain:
+            st = dg.dg_grouped_gemm_fp8(d["A"], d["sA"], d["B"], d["sB"], d["C"], d["offs"],
                                         p.G, p.M, p.N, p.K, code, sh)
         elif p.grouped:
-            st = dg.dg_grouped_gemm_fp8_ex(d["A"].data_ptr(), fa, d["sA"].data_ptr(), p.sa_rows,
-                                           d["B"].data_ptr(), fb, d["sB"].data_ptr(), d["C"].data_ptr(),
-                                           d["offs"].data_ptr(), p.G, p.M, p.N, p.K, code, sh)
+            st = dg.dg_grouped_gemm_fp8_ex(d["A"], fa, d["sA"], p.sa_rows, d["B"], fb, d["sB"], d["C"],
+                                           d["offs"], p.G, p.M, p.N, p.K, code, sh)
         elif plain:
-            st = dg.dg_gemm_fp8_blockscaled(d["A"].data_ptr(), d["sA"].data_ptr(), d["B"].data_ptr(),
-                                            d["sB"].data_ptr(), d["C"].data_ptr(), p.M, p.N, p.K,
-                                            code, sh)
+            st = dg.dg_gemm_fp8_blockscaled(d["A"], d["sA"], d["B"], d["sB"], d["C"], p.M, p.N, p.K, code, sh)
         else:
-            st = dg.dg_gemm_fp8_ex(d["A"].data_ptr(), fa, d["sA"].data_ptr(), p.sa_rows,
-                                   d["B"].data_ptr(), fb, d["sB"].data_ptr(),
-                                   d["C"].data_ptr(), p.M, p.N, p.K, code, sh)
+            st = dg.dg_gemm_fp8_ex(d["A"], fa, d["sA"], p.sa_rows, d["B"], fb, d["sB"], d["C"],
+                                   p.M, p.N, p.K, code, sh)
         if st != dg.DG_OK:
             raise dg.DGError(st, "bench step")
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
     K = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(K):
-        ev[i].record(stream)
-        step(args.warmup + i)
-    ev[K].record(stream)
-    torch.cuda.synchronize()
-    t_end = time.perf_counter()
-
-    ms_step = (t_end - t_start) * 1e3 / K
-    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(K)])
-    kern_ms = float(ev[0].elapsed_time(ev[K])) / K
-    log(f"kernel ms (HIP events): mean {kern_ms:.4f}  p10 {np.percentile(per, 10):.4f}  "
-        f"p50 {np.percentile(per, 50):.4f}  p90 {np.percentile(per, 90):.4f}; wall ms/step {ms_step:.4f}")
+    ms_step, kern_ms, _ = run_timed(step, K, args.warmup, not args.no_graph)
 
     flop = p.algorithmic_flop()
-    if args.workload in HBM_BOUND and args.workload == 3:
+    if args.workload in GBS_VALUE:
         value = step_bytes / (ms_step * 1e-3) / 1e9
         unit = "GB/s"
     else:
@@ -354,11 +376,12 @@ def main():
 
     cfg = {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "out_dtype": p.out_dtype,
            "scale_block": "128x128" if p.sa_rows == 128 else "A 1x128, B 128x128", "seed": p.seed,
-           "operand_copies": R}
+           "operand_copies": R, "launch": "eager" if args.no_graph else "hip_graph"}
     if p.a_fmt != "e4m3" or p.b_fmt != "e4m3":
         cfg.update({"a_fmt": p.a_fmt, "b_fmt": p.b_fmt})
     if p.grouped:
-        cfg.update({"groups": p.G, "real_rows": p.real_rows})
+        cfg.update({"groups": p.G, "real_rows": p.real_rows, "active_groups": p.active_groups(),
+                    "segments": "packed" if p.packed else "padded to 128 rows"})
     line = {"metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": K,
             "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None,

@@ -152,6 +152,43 @@ int dg_grouped_gemm_fp8_ex(const void* A, int a_fmt, const float* sA, int sa_row
                            int num_groups, int64_t M_total, int64_t N, int64_t K,
                            int out_dtype, hipStream_t stream);
 
+/*
+ * MoE grouped GEMM for few rows per expert (decode), over UNPADDED expert
+ * segments, in one launch.  MoE experts share N and K while the row count
+ * varies and is small at decode time (FP8-for-MoE page, section 2.2); many
+ * small GEMMs, whose launch cost rivals their run time, are better merged
+ * into one launch (same page, section 5.2).  Padding every expert's rows to
+ * 128 would multiply the work of a decode step many times over, so here the
+ * segments are packed: rows [o_e, o_{e+1}) of A and C belong to expert e for
+ * ANY 0 = o_0 <= o_1 <= ... <= o_G = M_total.  A scale block of 128 rows
+ * would then mix experts, so A carries one scale per row (the 1 x 128
+ * granularity of the FP8 kernel write-up, section 5.2):
+ *
+ *   A             : a_fmt bytes [M_total][K]
+ *   sA            : float32 [M_total][K/128]
+ *   B             : b_fmt bytes [num_groups][N][K]
+ *   sB            : float32 [num_groups][ceil(N/128)][K/128]
+ *   C             : [M_total][N] float32 or bfloat16
+ *   group_offsets : DEVICE int32 [num_groups + 1] as above
+ *
+ *   C[i][j] = sum_kb fp32(sA[i][kb] * sB_e[j/128][kb]) * P_kb[i][j] for i in
+ *   expert e's segment, P_kb as in dg_gemm_fp8_blockscaled with B_e.
+ *
+ * Tuned for segments of at most 64 rows: B_e is then streamed from HBM once
+ * and an expert without rows costs nothing but reading its two offsets.
+ * Longer segments are correct but re-stream B_e once per 64 rows (use
+ * dg_grouped_gemm_fp8 for prefill-sized segments).  Offsets are not
+ * validated on the host; the kernel clamps them into [0, M_total], so
+ * offsets that break the rules give wrong rows but no out-of-bounds access.
+ * Host-side errors: num_groups < 1, unknown formats -> DG_ERR_INVALID_ARG;
+ * the shared rules above otherwise (M_total need not be a multiple of 128).
+ */
+int dg_grouped_gemm_fp8_segments(const void* A, int a_fmt, const float* sA,
+                                 const void* B, int b_fmt, const float* sB,
+                                 void* C, const int32_t* group_offsets,
+                                 int num_groups, int64_t M_total, int64_t N, int64_t K,
+                                 int out_dtype, hipStream_t stream);
+
 typedef enum {
   DG_IN_F32 = 0,    /* X is float32 */
   DG_IN_BF16 = 1    /* X is bfloat16 */

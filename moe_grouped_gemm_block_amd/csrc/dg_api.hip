@@ -125,6 +125,30 @@ int launch_skinny(dg::GemmArgs a, int out_dtype, int combo, int row_sa, hipStrea
   return err == hipSuccess ? DG_OK : DG_ERR_LAUNCH;
 }
 
+// Unpadded expert segments: [NI 1/3][f32/bf16]
+struct SegSet { kfn t[2][2]; };
+#define DG_SEG_SET(SFX)                                                     \
+  {{{dg::dg_segments_n16_f32##SFX, dg::dg_segments_n16_bf16##SFX},          \
+    {dg::dg_segments_n48_f32##SFX, dg::dg_segments_n48_bf16##SFX}}}
+const SegSet kSeg[4] = {DG_SEG_SET(), DG_SEG_SET(_a4b5), DG_SEG_SET(_a5b4), DG_SEG_SET(_a5b5)};
+#undef DG_SEG_SET
+
+// One workgroup per (expert, column slab); the kernel picks the chunk height
+// per expert.  The slab width is 48 once that still gives every CU a
+// workgroup.
+int launch_segments(dg::GemmArgs a, int out_dtype, int combo, hipStream_t stream) {
+  const int wide = int64_t(a.G) * ((int64_t(a.N) + 47) / 48) >= kCUs ? 1 : 0;
+  const int cols = wide ? 48 : 16;
+  const int64_t slabs = (int64_t(a.N) + cols - 1) / cols;
+  const int64_t blocks = slabs * a.G;
+  if (blocks > INT32_MAX) return DG_ERR_UNSUPPORTED;
+  a.n_tiles = int(slabs);
+  void* kargs[] = {&a};
+  const void* fn = reinterpret_cast<const void*>(kSeg[combo].t[wide][out_dtype == DG_OUT_BF16 ? 1 : 0]);
+  hipError_t err = hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(256), kargs, 0, stream);
+  return err == hipSuccess ? DG_OK : DG_ERR_LAUNCH;
+}
+
 int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, int row_sa, hipStream_t stream) {
   const int combo = 2 * a_fmt + b_fmt;
   const TiledSet& ks = kTiled[combo];
@@ -217,6 +241,28 @@ int grouped_impl(const void* A, int a_fmt, const float* sA, int sa_rows, const v
 }  // namespace
 
 extern "C" {
+
+int dg_grouped_gemm_fp8_segments(const void* A, int a_fmt, const float* sA, const void* B, int b_fmt,
+                                 const float* sB, void* C, const int32_t* group_offsets, int num_groups,
+                                 int64_t M_total, int64_t N, int64_t K, int out_dtype, hipStream_t stream) {
+  if (!valid_fmt(a_fmt) || !valid_fmt(b_fmt)) return DG_ERR_INVALID_ARG;
+  if (num_groups < 1) return DG_ERR_INVALID_ARG;
+  int st = check_common(A, sA, B, sB, C, M_total, N, K, out_dtype);
+  if (st != DG_OK || M_total == 0 || N == 0) return st;
+  if (group_offsets == nullptr || !aligned(group_offsets, 4)) return DG_ERR_INVALID_ARG;
+  dg::GemmArgs a{};
+  a.A = static_cast<const uint8_t*>(A);
+  a.sA = sA;
+  a.B = static_cast<const uint8_t*>(B);
+  a.sB = sB;
+  a.C = C;
+  a.offs = group_offsets;
+  a.G = num_groups;
+  a.M = int(M_total);
+  a.N = int(N);
+  a.K = int(K);
+  return launch_segments(a, out_dtype, 2 * a_fmt + b_fmt, stream);
+}
 
 int dg_gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const float* sB,
                             void* C, int64_t M, int64_t N, int64_t K, int out_dtype,

@@ -23,9 +23,30 @@
 
 namespace dg {
 
-// ROW_SA: sA holds one scale per row and K-block ([M][K/128]).
+// One few-rows problem: rows [0, M) of A / sA / C, one expert's B and sB.
+struct SkinnyJob {
+  const uint8_t* A;       // [M][K]
+  const float* sA;        // [1][K/128] (one row block), or [M][K/128] with ROW_SA
+  const uint8_t* B;       // [N][K]
+  const float* sB;        // [ceil(N/128)][K/128]
+  void* C;                // [M][N]
+  int M, N, K;
+};
+
+// LDS bytes of gemm_skinny_body: per wave A in 2 stages, B in 3, row scales
+// in 2; reused for the partial sums of the final reduction.
+template <int MI, int NI, bool ROW_SA>
+constexpr int skinny_lds_bytes() {
+  constexpr int wave = 2 * 16 * MI * KBLK + 3 * 16 * NI * KBLK + (ROW_SA ? 2 * 256 : 0);
+  constexpr int red = 4 * 16 * MI * 16 * NI * 4;
+  return 4 * wave > red ? 4 * wave : red;
+}
+
+// The 16*NI columns from n0 of a few-rows problem, in the workgroup's LDS
+// buffer `lds` (skinny_lds_bytes bytes, 16-byte aligned).  ROW_SA: sA holds
+// one scale per row and K-block ([M][K/128]).
 template <int MI, int NI, bool OUT_BF16, int FA = FMT_E4M3, int FB = FMT_E4M3, bool ROW_SA = false>
-__device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p) {
+__device__ __forceinline__ void gemm_skinny_body(const SkinnyJob& p, const int n0, uint8_t* lds) {
   constexpr int NW = 4;                         // waves, each a quarter of the K-blocks
   constexpr int RM = 16 * MI, CN = 16 * NI;     // rows / columns of the workgroup tile
   constexpr int A_BYTES = RM * KBLK, B_BYTES = CN * KBLK;
@@ -33,14 +54,10 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p) {
   constexpr int WAVE_LDS = 2 * A_BYTES + 3 * B_BYTES + 2 * S_BYTES;   // A: 2 stages, B: 3, sA: 2
   constexpr int A_CH = RM / 8, B_CH = CN / 8;   // 1 KB copy chunks per K-block
   constexpr int A_OPS = A_CH + (ROW_SA ? 1 : 0); // A copy instructions per K-block (+ its row scales)
-  constexpr int RED = NW * RM * CN * 4;         // partial sums for the reduction
-  constexpr int LDS_BYTES = (NW * WAVE_LDS > RED) ? NW * WAVE_LDS : RED;
   static_assert(2 * B_CH + A_OPS < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = blockIdx.x * CN;
   const int M = p.M, N = p.N, K = p.K;
   const int Kb = K / KBLK;
   const int Nb = (N + KBLK - 1) / KBLK;
@@ -203,8 +220,54 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p) {
   }
 }
 
+template <int MI, int NI, bool OUT_BF16, int FA, int FB, bool ROW_SA>
+__device__ __forceinline__ void gemm_skinny_dense(const GemmArgs& p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[skinny_lds_bytes<MI, NI, ROW_SA>()];
+  const SkinnyJob j{p.A, p.sA, p.B, p.sB, p.C, p.M, p.N, p.K};
+  gemm_skinny_body<MI, NI, OUT_BF16, FA, FB, ROW_SA>(j, int(blockIdx.x) * 16 * NI, lds);
+}
+
+// Grouped GEMM over unpadded expert segments (rows [o_e, o_{e+1}) of A and C
+// belong to expert e, any o_e), one A scale per row.  Workgroup b takes
+// expert e = b / n_tiles and column slab b % n_tiles.  The chunk height is
+// chosen per expert from its row count (16, 32 or 64 rows, a uniform branch),
+// so an expert with at most 64 rows streams its slab of B_e exactly once;
+// longer segments are walked in chunks of 64 rows, each streaming the slab
+// again.  Experts without rows cost two offset reads.  Offsets are clamped to
+// [0, M] so that inconsistent offsets cannot address outside A or C.
+template <int NI, bool OUT_BF16, int FA, int FB>
+__device__ __forceinline__ void gemm_skinny_segments(const GemmArgs& p) {
+  constexpr int L1 = skinny_lds_bytes<1, NI, true>(), L2 = skinny_lds_bytes<2, NI, true>();
+  constexpr int L4 = skinny_lds_bytes<4, NI, true>();
+  constexpr int L12 = L1 > L2 ? L1 : L2;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[L12 > L4 ? L12 : L4];
+  const int e = int(blockIdx.x) / p.n_tiles;
+  const int n0 = (int(blockIdx.x) - e * p.n_tiles) * 16 * NI;
+  typedef const __attribute__((address_space(4))) int32_t cint;
+  const int lo = min(max(int(((cint*)p.offs)[e]), 0), p.M);
+  const int hi = min(max(int(((cint*)p.offs)[e + 1]), lo), p.M);
+  const int N = p.N, K = p.K, Kb = K / KBLK, Nb = (N + KBLK - 1) / KBLK;
+  const size_t c_row = size_t(N) * (OUT_BF16 ? 2 : 4);
+  auto job = [&](int r0, int rows) {
+    return SkinnyJob{p.A + size_t(r0) * K, p.sA + size_t(r0) * Kb, p.B + size_t(e) * N * K,
+                     p.sB + size_t(e) * Nb * Kb, static_cast<uint8_t*>(p.C) + size_t(r0) * c_row, rows, N, K};
+  };
+  const int len = hi - lo;
+  if (len <= 0) return;
+  if (len <= 16) {
+    gemm_skinny_body<1, NI, OUT_BF16, FA, FB, true>(job(lo, len), n0, lds);
+  } else if (len <= 32) {
+    gemm_skinny_body<2, NI, OUT_BF16, FA, FB, true>(job(lo, len), n0, lds);
+  } else {
+    for (int r0 = lo; r0 < hi; r0 += 64) {
+      if (r0 != lo) __syncthreads();           // LDS of the previous chunk's reduction is free
+      gemm_skinny_body<4, NI, OUT_BF16, FA, FB, true>(job(r0, min(hi - r0, 64)), n0, lds);
+    }
+  }
+}
+
 #define DG_SKINNY_KERNEL(NAME, MI, NI, BF16, FA, FB, RS) \
-  __global__ __launch_bounds__(256, 1) void NAME(GemmArgs p) { gemm_skinny_body<MI, NI, BF16, FA, FB, RS>(p); }
+  __global__ __launch_bounds__(256, 1) void NAME(GemmArgs p) { gemm_skinny_dense<MI, NI, BF16, FA, FB, RS>(p); }
 #define DG_SKINNY_SHAPE(ROWS, COLS, MI, NI, SFX, FA, FB, RS)                                \
   DG_SKINNY_KERNEL(dg_skinny_m##ROWS##_n##COLS##_bf16##SFX, MI, NI, true, FA, FB, RS)       \
   DG_SKINNY_KERNEL(dg_skinny_m##ROWS##_n##COLS##_f32##SFX, MI, NI, false, FA, FB, RS)
@@ -220,6 +283,20 @@ DG_SKINNY_FORMATS(_a5b5, FMT_E5M2, FMT_E5M2)
 DG_SKINNY_FORMATS(_a4b5, FMT_E4M3, FMT_E5M2)
 DG_SKINNY_FORMATS(_a5b4, FMT_E5M2, FMT_E4M3)
 #undef DG_SKINNY_FORMATS
+
+#define DG_SEG_KERNEL(NAME, NI, BF16, FA, FB) \
+  __global__ __launch_bounds__(256, 1) void NAME(GemmArgs p) { gemm_skinny_segments<NI, BF16, FA, FB>(p); }
+#define DG_SEG_SHAPE(COLS, NI, SFX, FA, FB)                              \
+  DG_SEG_KERNEL(dg_segments_n##COLS##_bf16##SFX, NI, true, FA, FB)       \
+  DG_SEG_KERNEL(dg_segments_n##COLS##_f32##SFX, NI, false, FA, FB)
+#define DG_SEG_FORMATS(SFX, FA, FB) DG_SEG_SHAPE(48, 3, SFX, FA, FB) DG_SEG_SHAPE(16, 1, SFX, FA, FB)
+DG_SEG_FORMATS(, FMT_E4M3, FMT_E4M3)
+DG_SEG_FORMATS(_a5b5, FMT_E5M2, FMT_E5M2)
+DG_SEG_FORMATS(_a4b5, FMT_E4M3, FMT_E5M2)
+DG_SEG_FORMATS(_a5b4, FMT_E5M2, FMT_E4M3)
+#undef DG_SEG_FORMATS
+#undef DG_SEG_SHAPE
+#undef DG_SEG_KERNEL
 #undef DG_SKINNY_ROWS
 #undef DG_SKINNY_SHAPE
 #undef DG_SKINNY_KERNEL

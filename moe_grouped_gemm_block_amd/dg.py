@@ -29,7 +29,8 @@ DG_ERR_UNSUPPORTED = -2
 DG_ERR_LAUNCH = -3
 
 EXPORTED = ("dg_gemm_fp8_blockscaled", "dg_grouped_gemm_fp8", "dg_gemm_fp8_ex",
-            "dg_grouped_gemm_fp8_ex", "dg_quantize_fp8_blockscaled", "dg_status_string")
+            "dg_grouped_gemm_fp8_ex", "dg_grouped_gemm_fp8_segments", "dg_quantize_fp8_blockscaled",
+            "dg_status_string")
 
 _lib = None
 
@@ -52,6 +53,8 @@ def lib() -> ctypes.CDLL:
         L.dg_gemm_fp8_ex.restype = ci
         L.dg_grouped_gemm_fp8_ex.argtypes = [vp, ci, vp, ci, vp, ci, vp, vp, vp, ci, i64, i64, i64, ci, vp]
         L.dg_grouped_gemm_fp8_ex.restype = ci
+        L.dg_grouped_gemm_fp8_segments.argtypes = [vp, ci, vp, vp, ci, vp, vp, vp, ci, i64, i64, i64, ci, vp]
+        L.dg_grouped_gemm_fp8_segments.restype = ci
         L.dg_quantize_fp8_blockscaled.argtypes = [vp, ci, vp, vp, i64, i64, ci, vp]
         L.dg_quantize_fp8_blockscaled.restype = ci
         L.dg_status_string.argtypes = [ci]
@@ -80,6 +83,12 @@ def dg_grouped_gemm_fp8_ex(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, group_offsets
                            N, K, out_dtype, stream) -> int:
     return lib().dg_grouped_gemm_fp8_ex(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, group_offsets, num_groups,
                                         M_total, N, K, out_dtype, stream)
+
+
+def dg_grouped_gemm_fp8_segments(A, a_fmt, sA, B, b_fmt, sB, C, group_offsets, num_groups, M_total, N, K,
+                                 out_dtype, stream) -> int:
+    return lib().dg_grouped_gemm_fp8_segments(A, a_fmt, sA, B, b_fmt, sB, C, group_offsets, num_groups,
+                                              M_total, N, K, out_dtype, stream)
 
 
 def dg_quantize_fp8_blockscaled(X, in_dtype, Q, S, M, K, block_rows, stream) -> int:
@@ -219,6 +228,32 @@ def grouped_gemm_fp8(A, sA, B, sB, group_offsets, out_dtype="bf16", C=None, stre
                                     _stream(stream))
     if st != DG_OK:
         raise DGError(st, "dg_grouped_gemm_fp8")
+    return C
+
+
+def grouped_gemm_fp8_segments(A, sA, B, sB, group_offsets, out_dtype="bf16", C=None, stream=None,
+                              a_fmt="e4m3", b_fmt="e4m3"):
+    """MoE grouped GEMM over packed (unpadded) expert segments with one A
+    scale per row, sA [M_total][K/128]; meant for few rows per expert."""
+    torch = _torch()
+    _check_fp8(A, "A")
+    _check_fp8(B, "B")
+    M_total, K = A.shape
+    G, N, K2 = B.shape
+    if K != K2:
+        raise ValueError("A and B must share K")
+    _check_f32(sA, "sA", (M_total, K // 128))
+    _check_f32(sB, "sB", (G, -(-N // 128), K // 128))
+    if (group_offsets.dtype != torch.int32 or not group_offsets.is_cuda
+            or tuple(group_offsets.shape) != (G + 1,)):
+        raise ValueError("group_offsets must be a device int32 tensor of G + 1 entries")
+    code = out_code(out_dtype)
+    C = _out(C, M_total, N, code, A)
+    st = dg_grouped_gemm_fp8_segments(A.data_ptr(), fmt_code(a_fmt), sA.data_ptr(), B.data_ptr(),
+                                      fmt_code(b_fmt), sB.data_ptr(), C.data_ptr(), group_offsets.data_ptr(),
+                                      G, M_total, N, K, code, _stream(stream))
+    if st != DG_OK:
+        raise DGError(st, "dg_grouped_gemm_fp8_segments")
     return C
 
 

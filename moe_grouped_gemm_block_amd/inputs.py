@@ -170,6 +170,7 @@ class Problem:
     a_fmt: str = "e4m3"                 # code format of A / B: "e4m3" or "e5m2"
     b_fmt: str = "e4m3"
     sa_rows: int = BLOCK                # rows per A scale block: 128 or 1 (per token)
+    packed: bool = False                # grouped segments not padded to 128 rows
 
     @property
     def grouped(self) -> bool:
@@ -186,11 +187,18 @@ class Problem:
     def padded_flop(self) -> int:
         return 2 * self.M * self.N * self.K
 
+    def active_groups(self) -> int:
+        """Experts with at least one row (all of them for a dense problem)."""
+        if self.group_offsets is None:
+            return 1
+        return int(np.count_nonzero(np.diff(self.group_offsets)))
+
     def algorithmic_bytes(self) -> int:
-        """A + B + sA + sB read once, C written once."""
+        """A + sA + the B and sB of experts that have rows, read once; C written once."""
         cbytes = 4 if self.out_dtype == "f32" else 2
-        return (self.A.nbytes + self.B.nbytes + self.sA.nbytes + self.sB.nbytes
-                + self.M * self.N * cbytes
+        G = max(self.G, 1)
+        b = (self.B.nbytes + self.sB.nbytes) // G * self.active_groups()
+        return (self.A.nbytes + self.sA.nbytes + b + self.M * self.N * cbytes
                 + (0 if self.group_offsets is None else self.group_offsets.nbytes))
 
 
@@ -270,10 +278,10 @@ def grouped_problem(G: int, N: int, K: int, T: int, seed: int,
 
 
 def route(G: int, T: int, rng: np.random.Generator, popularity: str = "uniform",
-          zipf_s: float = 1.1, zero_lowest: int = 4):
+          zipf_s: float = 1.1, zero_lowest: int = 4, pad: int = BLOCK):
     """Top-2 routing of T tokens over G experts -> (offsets int64 [G+1],
     per-expert token ids, per-expert token counts).  Segments are padded to
-    multiples of 128 rows."""
+    multiples of `pad` rows (1: packed)."""
     if popularity == "uniform":
         w = np.ones(G)
     elif popularity == "zipf":
@@ -293,14 +301,36 @@ def route(G: int, T: int, rng: np.random.Generator, popularity: str = "uniform",
         toks = np.nonzero((top == e).any(axis=1))[0]      # token-id order
         seg_tokens.append(toks)
         counts[e] = len(toks)
-    padded = -(-counts // BLOCK) * BLOCK
+    padded = -(-counts // pad) * pad
     offsets = np.zeros(G + 1, np.int64)
     offsets[1:] = np.cumsum(padded)
     return offsets, seg_tokens, counts
 
 
+def decode_problem(G: int, N: int, K: int, T: int, seed: int, popularity: str = "zipf",
+                   zipf_s: float = 1.1, zero_lowest: int = 4, b_std: float = 0.02,
+                   out_dtype: str = "bf16", name: str = "decode") -> Problem:
+    """MoE expert GEMM of one decode step: T tokens, top-2 routing, packed
+    segments (no padding rows) and one A scale per token and 128 columns.
+    Same distributions as grouped_problem."""
+    r_act, r_w, _, r_route = streams(seed)
+    X = r_act.standard_normal((T, K), dtype=np.float32)
+    Bq = np.empty((G, N, K), np.uint8)
+    sB = np.empty((G, -(-N // BLOCK), K // BLOCK), np.float32)
+    for e in range(G):
+        Be = r_w.standard_normal((N, K), dtype=np.float32) * np.float32(b_std)
+        Bq[e], sB[e] = quantize(Be)
+        del Be
+    offsets, seg_tokens, counts = route(G, T, r_route, popularity, zipf_s, zero_lowest, pad=1)
+    A = np.concatenate([X[t] for t in seg_tokens], axis=0) if T else np.zeros((0, K), np.float32)
+    qA, sA = quantize(A, rows=1)
+    return Problem(name=name, A=qA, sA=sA, B=Bq, sB=sB, M=int(offsets[-1]), N=N, K=K,
+                   out_dtype=out_dtype, seed=seed, group_offsets=offsets.astype(np.int32),
+                   real_rows=int(counts.sum()), sa_rows=1, packed=True)
+
+
 # ---------------------------------------------------------------------------
-# The five named workloads
+# The named workloads
 # ---------------------------------------------------------------------------
 
 CONFIG_NAMES = {
@@ -309,11 +339,14 @@ CONFIG_NAMES = {
     3: "skinny_m64_n12288_k4096_bf16",
     4: "moe_g8_n4096_k4096_uniform_bf16",
     5: "moe_g64_n2048_k2048_zipf_bf16",
+    6: "moe_decode_g64_n2048_k2048_t128_zipf_bf16",
 }
 
 
 def make_config(i: int, seed: int | None = None, fmt: str = "e4m3", sa_rows: int = BLOCK) -> Problem:
-    """Workload i (1..5); the default seed is the workload index.  fmt =
+    """Workload i (1..6); the default seed is the workload index.  Workload 6,
+    a decode step of the MoE of workload 5 (128 tokens, packed segments,
+    per-token A scales), always has sa_rows = 1.  fmt =
     "e5m2" quantises both operands of the dense workloads 1-3 to E5M2
     instead (same data, name suffixed with _e5m2).  sa_rows = 1 gives A one
     scale per token and 128 columns (name suffixed with _a1x128)."""
@@ -336,4 +369,6 @@ def make_config(i: int, seed: int | None = None, fmt: str = "e4m3", sa_rows: int
     if i == 5:
         return grouped_problem(64, 2048, 2048, 8192, s, popularity="zipf",
                                name=CONFIG_NAMES[5] + sfx, sa_rows=sa_rows)
+    if i == 6:
+        return decode_problem(64, 2048, 2048, 128, s, popularity="zipf", name=CONFIG_NAMES[6])
     raise ValueError(f"unknown workload {i}")

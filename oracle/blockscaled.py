@@ -167,7 +167,9 @@ def grouped_gemm(A: np.ndarray, sA: np.ndarray, B: np.ndarray, sB: np.ndarray,
 
     A: uint8 [M_total][K]; sA: fp32 [M_total/sa_rows][K/128] (sa_rows 128 or 1)
     B: uint8 [G][N][K];    sB: fp32 [G][ceil(N/128)][K/128]
-    group_offsets: int [G+1], rows [o_e, o_{e+1}) belong to expert e.
+    group_offsets: int [G+1], rows [o_e, o_{e+1}) belong to expert e; the o_e
+    are multiples of 128 for 128-row A scale blocks and arbitrary for sa_rows = 1
+    (packed segments, as in a decode step with few tokens per expert).
     Each expert's rows are a dense product with that expert's B and sB.
     """
     M_total = A.shape[0]
@@ -186,9 +188,10 @@ def grouped_gemm(A: np.ndarray, sA: np.ndarray, B: np.ndarray, sB: np.ndarray,
         if len(sel) == 0:
             continue
         local = rows[sel] - lo
-        # the expert's A scale rows start at block lo / sa_rows
-        if lo % BLOCK:
-            raise ValueError("segment starts must be multiples of 128")
+        # the expert's A scale rows start at block lo / sa_rows; with one scale
+        # per row a segment may start anywhere (packed segments)
+        if lo % sa_rows:
+            raise ValueError("with 128-row A scale blocks, segment starts must be multiples of 128")
         sA_e = sA[lo // sa_rows:(hi + sa_rows - 1) // sa_rows]
         Ce, me = gemm_blockscaled(A[lo:hi], sA_e, B[e], sB[e], rows=local, cols=cols,
                                   a_fmt=a_fmt, b_fmt=b_fmt, sa_rows=sa_rows)

@@ -128,6 +128,23 @@ def test_general_entry_points_reject_scale_granularity(L, rows):
     assert dense_ex(0, 0, rows, M=0) == INVALID        # checked before the empty-work shortcut
 
 
+def segments(fa=0, fb=0, **kw):
+    d = dict(A=P, sA=P, B=P, sB=P, C=P, offs=P, G=4, M=300, N=256, K=256, out=1)
+    d.update(kw)
+    return dg.dg_grouped_gemm_fp8_segments(d["A"], fa, d["sA"], d["B"], fb, d["sB"], d["C"], d["offs"],
+                                           d["G"], d["M"], d["N"], d["K"], d["out"], None)
+
+
+@pytest.mark.parametrize("fa,fb,kw,want", [
+    (2, 0, {}, INVALID), (0, 5, {}, INVALID), (0, 0, dict(G=0), INVALID), (0, 0, dict(G=-1), INVALID),
+    (0, 0, dict(offs=None), INVALID), (0, 0, dict(offs=P + 2), INVALID), (0, 0, dict(A=None), INVALID),
+    (0, 0, dict(sA=P + 1), INVALID), (1, 1, dict(out=9), INVALID), (0, 0, dict(M=-5), INVALID),
+    (0, 0, dict(K=100), UNSUP), (0, 0, dict(N=20), UNSUP), (0, 0, dict(M=0), OK), (1, 0, dict(N=0), OK),
+])
+def test_segments_validation(L, fa, fb, kw, want):
+    assert segments(fa, fb, **kw) == want
+
+
 def quant(X=P, dt=1, Q=P, S=P, M=256, K=256, R=128):
     return dg.dg_quantize_fp8_blockscaled(X, dt, Q, S, M, K, R, None)
 

@@ -151,3 +151,24 @@ def test_e5m2_problem_blocks_reach_the_format_max():
                 blk = X[rb * 128:(rb + 1) * 128, kb * 128:(kb + 1) * 128]
                 assert np.abs(tab[blk]).max() == 57344.0
     assert p.a_fmt == "e5m2" and p.b_fmt == "e5m2"
+
+
+def test_decode_workload_is_packed_top2():
+    """Workload 6: 128 tokens, two distinct experts each, segments packed with
+    no padding rows, one A scale per row, some experts empty."""
+    p = I.make_config(6)
+    offs = p.group_offsets.astype(np.int64)
+    counts = np.diff(offs)
+    assert p.packed and p.sa_rows == 1
+    assert offs[0] == 0 and offs[-1] == p.M == 2 * 128 == p.real_rows
+    assert np.all(counts >= 0) and np.any(counts == 0) and counts.max() <= 64
+    assert p.sA.shape == (p.M, p.K // 128) and p.A.shape == (p.M, p.K)
+    assert p.active_groups() == np.count_nonzero(counts)
+    # a quantised row is the same token wherever it appears: each token's row
+    # occurs in exactly two segments
+    rows = {}
+    for e in range(p.G):
+        for r in range(offs[e], offs[e + 1]):
+            rows.setdefault(p.A[r].tobytes(), []).append(e)
+    assert all(len(v) == 2 and v[0] != v[1] for v in rows.values())
+    assert len(rows) == 128

@@ -124,3 +124,37 @@ def test_planted_block_index_slip_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "gemm_blockscaled", slipped)
     with pytest.raises(AssertionError):
         test_brute_force_row_scales(5, 4, 128, 0)
+
+
+def test_packed_segments_are_per_expert_dense_products():
+    """Segments that start anywhere (no padding rows), per-row A scales: every
+    expert's rows are the dense product with that expert's B, and rows of a
+    segment never see another expert's weights."""
+    rng = np.random.default_rng(6)
+    offs = np.array([0, 3, 3, 20, 21, 85], np.int64)          # 3, 0, 17, 1, 64 rows
+    G, N, K = 5, 24, 256
+    A = codes(rng, (85, K))
+    sA = np.exp2(rng.uniform(-5, 5, (85, K // 128))).astype(np.float32)
+    B = codes(rng, (G, N, K))
+    sB = np.exp2(rng.uniform(-5, 5, (G, 1, K // 128))).astype(np.float32)
+    C, _ = oracle.grouped_gemm(A, sA, B, sB, offs, sa_rows=1)
+    for e in range(G):
+        lo, hi = offs[e], offs[e + 1]
+        if hi > lo:
+            Ce, _ = oracle.gemm_blockscaled(A[lo:hi], sA[lo:hi], B[e], sB[e], sa_rows=1)
+            np.testing.assert_array_equal(C[lo:hi], Ce)
+    # brute force on one row of each non-empty segment
+    for i in (0, 2, 3, 19, 20, 21, 84):
+        e = int(np.searchsorted(offs, i, side="right") - 1)
+        Ce, me = exact_rowscaled(A[i:i + 1], sA[i:i + 1], B[e], sB[e])
+        for j in range(N):
+            err = abs(Fraction(float(C[i, j])) - Ce[0][j])
+            assert err <= Fraction(5) * Fraction(U53) * me[0][j], (i, j)
+
+
+def test_packed_segments_need_row_scales():
+    A = np.zeros((10, 128), np.uint8)
+    B = np.zeros((2, 8, 128), np.uint8)
+    sB = np.ones((2, 1, 1), np.float32)
+    with pytest.raises(ValueError):
+        oracle.grouped_gemm(A, np.ones((1, 1), np.float32), B, sB, np.array([0, 3, 10]))
