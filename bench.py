@@ -74,8 +74,9 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(workload_name: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary,
-    or None when it is missing or was taken on other kernel sources."""
+    """HBM bytes per step (all launches of one step) from the committed
+    rocprofv3 counter summary, or None when it is missing or was taken on
+    other kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         rec = json.load(open(path))[workload_name]
@@ -83,7 +84,7 @@ def measured_traffic(workload_name: str):
         return None
     if rec.get("kernel_hash") != kernel_source_hash():
         return None
-    return int(rec["hbm_bytes_per_launch"])
+    return int(rec["hbm_bytes_per_step"])
 
 
 def cpu_baseline(p, target_s: float = 12.0):
