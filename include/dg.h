@@ -23,8 +23,8 @@
  *   A  : E4M3 bytes, [M][K] row-major (K contiguous)
  *   B  : E4M3 bytes, [N][K] row-major, i.e. the K x N operand stored
  *        column-major (K contiguous)
- *   sA : float32 [ceil(M/128)][K/128] row-major
- *   sB : float32 [ceil(N/128)][K/128] row-major
+ *   sA : float32 [ceil(M/128)][Kb] row-major, Kb = ceil(K/128)
+ *   sB : float32 [ceil(N/128)][Kb] row-major
  *   C  : [M][N] row-major, float32 or bfloat16 (out_dtype)
  *
  * Conventions shared by every entry point:
@@ -42,7 +42,12 @@
  *     out_dtype, A / B / C not 16-byte aligned, sA / sB / group_offsets not
  *     4-byte aligned.
  *   - Shapes outside the supported set return DG_ERR_UNSUPPORTED: K must be a
- *     multiple of 128 and at most 2^22, N a multiple of 8.  M is arbitrary.
+ *     multiple of 16 (so that every row of A and B starts 16-byte aligned)
+ *     and at most 2^22.  M and N are arbitrary.
+ *   - Kb = ceil(K/128) K-blocks.  When K is not a multiple of 128 the last
+ *     K-block is partial: its P_kb sums the K - 128 (Kb - 1) remaining
+ *     columns and its scales are those of that partial block (the scale
+ *     arrays have Kb columns).
  *   - Empty work (M == 0 or N == 0) is a no-op that returns DG_OK.  K == 0
  *     writes zeros.
  *   - A failed kernel launch returns DG_ERR_LAUNCH.  Faults inside a kernel
@@ -88,9 +93,9 @@ int dg_gemm_fp8_blockscaled(const void* A, const float* sA,
  * the row count varies, FP8-for-MoE page, section 2.2).
  *
  *   A             : E4M3 [M_total][K]; rows [o_e, o_{e+1}) belong to expert e
- *   sA            : float32 [M_total/128][K/128]
+ *   sA            : float32 [M_total/128][Kb]
  *   B             : E4M3 [num_groups][N][K] (expert e's B_e, K contiguous)
- *   sB            : float32 [num_groups][ceil(N/128)][K/128]
+ *   sB            : float32 [num_groups][ceil(N/128)][Kb]
  *   C             : [M_total][N] float32 or bfloat16
  *   group_offsets : DEVICE int32 [num_groups + 1] with
  *                   0 = o_0 <= o_1 <= ... <= o_G = M_total, every o_e a
@@ -131,7 +136,7 @@ typedef enum {
  *                  128-wide K-block, the 1 x 128 granularity of the FP8 kernel
  *                  write-up's section 5.2 table, which
  *                  dg_quantize_fp8_blockscaled(block_rows = 1) produces:
- *                    sA : float32 [M][K/128] row-major (grouped: [M_total][K/128])
+ *                    sA : float32 [M][Kb] row-major (grouped: [M_total][Kb])
  *                  and C[i][j] takes fp32(sA[i][kb] * sB[j/128][kb]) as the
  *                  factor of P_kb[i][j].  B keeps its 128 x 128 blocks.
  *
@@ -165,9 +170,9 @@ int dg_grouped_gemm_fp8_ex(const void* A, int a_fmt, const float* sA, int sa_row
  * granularity of the FP8 kernel write-up, section 5.2):
  *
  *   A             : a_fmt bytes [M_total][K]
- *   sA            : float32 [M_total][K/128]
+ *   sA            : float32 [M_total][Kb]
  *   B             : b_fmt bytes [num_groups][N][K]
- *   sB            : float32 [num_groups][ceil(N/128)][K/128]
+ *   sB            : float32 [num_groups][ceil(N/128)][Kb]
  *   C             : [M_total][N] float32 or bfloat16
  *   group_offsets : DEVICE int32 [num_groups + 1] as above
  *

@@ -45,6 +45,50 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return bf16_bits(lo) | (bf16_bits(hi) << 16);
 }
 
+// Buffer offset that lies past any buffer's end (num_records <= 2^31 here):
+// a load from it returns zeros.  Row offsets below 2^31 can be added to it
+// without wrapping.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// Store the W consecutive output values v[0 .. W) of one row at columns
+// n0 .. n0 + W - 1 of C (row-major, N columns; `row_off` = row * N elements),
+// skipping columns >= N.  When every row starts 16-byte aligned (N % 8 == 0
+// for BF16, N % 4 == 0 for FP32) whole 16-byte vectors are stored; otherwise
+// element by element (a uniform branch on N).
+template <bool OUT_BF16, int W>
+__device__ __forceinline__ void store_row_span(void* C, size_t row_off, int n0, int N, const float* v) {
+  constexpr int VEC = OUT_BF16 ? 8 : 4;             // elements per 16 bytes
+  static_assert(W % VEC == 0, "span of whole vectors");
+  if (N % VEC == 0) {
+#pragma unroll
+    for (int c = 0; c < W / VEC; ++c) {
+      const int n = n0 + VEC * c;
+      if (n >= N) continue;                           // whole vector in or out
+      if constexpr (OUT_BF16) {
+        uint4 w;
+        w.x = pack_bf16x2(v[8 * c + 0], v[8 * c + 1]);
+        w.y = pack_bf16x2(v[8 * c + 2], v[8 * c + 3]);
+        w.z = pack_bf16x2(v[8 * c + 4], v[8 * c + 5]);
+        w.w = pack_bf16x2(v[8 * c + 6], v[8 * c + 7]);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(C) + row_off + n) = w;
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(C) + row_off + n) =
+            float4{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
+      }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < W; ++t) {
+      const int n = n0 + t;
+      if (n >= N) continue;
+      if constexpr (OUT_BF16)
+        static_cast<uint16_t*>(C)[row_off + n] = uint16_t(bf16_bits(v[t]));
+      else
+        static_cast<float*>(C)[row_off + n] = v[t];
+    }
+  }
+}
+
 // 16-byte granule swizzle inside a 128-byte LDS row: row r's granule g is
 // stored at slot g ^ ((r ^ (r >> 3)) & 7).  Eight consecutive rows, and the
 // two 8-row halves of sixteen consecutive rows, then hit distinct slots, so

@@ -34,7 +34,9 @@ int check_common(const void* A, const float* sA, const void* B, const float* sB,
     if (!aligned(A, 16) || !aligned(B, 16) || !aligned(sA, 4) || !aligned(sB, 4))
       return DG_ERR_INVALID_ARG;
   }
-  if (K % dg::KBLK != 0 || N % 8 != 0) return DG_ERR_UNSUPPORTED;
+  // rows of A and B must start 16-byte aligned (16-byte copies); the last
+  // K-block may be partial, any N is fine
+  if (K % 16 != 0) return DG_ERR_UNSUPPORTED;
   if (K > kMaxK) return DG_ERR_UNSUPPORTED;
   return DG_OK;
 }
@@ -166,7 +168,8 @@ int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, int row_s
   bool use512 = a.N > 256 && wide >= kCUs / 2;
   if (forced_tile() == 512) use512 = true;
   if (forced_tile() == 256) use512 = false;
-  if (forced_tile() == 1512 && combo == 0)       // the 1 x 8 variant exists for E4M3 x E4M3
+  // the 1 x 8 variant exists for E4M3 x E4M3 without K or N tails
+  if (forced_tile() == 1512 && combo == 0 && a.K % dg::KBLK == 0 && a.N % 8 == 0)
     return launch_tiles(a, 512, 512, dg::dg_gemm_wide_128x512_bf16, dg::dg_gemm_wide_128x512_f32, out_dtype,
                         stream);
   if (use512 && forced_tile() == 0 && tail_tile() != 0) {
@@ -316,7 +319,8 @@ const char* dg_status_string(int status) {
   switch (status) {
     case DG_OK: return "DG_OK: success";
     case DG_ERR_INVALID_ARG: return "DG_ERR_INVALID_ARG: invalid argument (null, misaligned, negative or oversized)";
-    case DG_ERR_UNSUPPORTED: return "DG_ERR_UNSUPPORTED: shape not supported (K % 128 != 0, N % 8 != 0 or K > 2^22)";
+    case DG_ERR_UNSUPPORTED:
+      return "DG_ERR_UNSUPPORTED: shape not supported (GEMM: K % 16 != 0 or K > 2^22; quantiser: K % 128 != 0)";
     case DG_ERR_LAUNCH: return "DG_ERR_LAUNCH: kernel launch failed";
     default: return "unknown dg_status";
   }

@@ -218,7 +218,7 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   tile_of<8>(blockIdx.x, p.m_tiles, p.n_tiles, tm, tn);
   const int m0 = (p.m_tile0 + tm) * BM, n0 = tn * BN;
   const int M = p.M, N = p.N, K = p.K;
-  const int Kb = K / KBLK;
+  const int Kb = (K + KBLK - 1) / KBLK;          // the last K-block may be partial
   const int Nb = (N + KBLK - 1) / KBLK;
 
   int e = 0;
@@ -271,8 +271,11 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
         copy4_to_lds(rS, s_lane + uint32_t(kb * 4),
                      lds_addr + uint32_t(2 * (A_BYTES + B_BYTES) + stage * SA_BYTES + wave * 256));
     }
-    const uint32_t a_kb = opaque(a_lane + uint32_t(kb * KBLK));
-    const uint32_t b_kb = opaque(b_lane + uint32_t(kb * KBLK));
+    // a granule past K (partial last K-block) reads as zeros: its offset is
+    // pushed past the buffer end (all offsets stay below 2^32)
+    const bool k_in = kb * KBLK + gsl < K;
+    const uint32_t a_kb = opaque(k_in ? a_lane + uint32_t(kb * KBLK) : kOutOfRange);
+    const uint32_t b_kb = opaque(k_in ? b_lane + uint32_t(kb * KBLK) : kOutOfRange);
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int c = wave + NW * i;
@@ -424,28 +427,7 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[ni * 4 + r] = acc[mi][ni][r];
-    if constexpr (OUT_BF16) {
-      uint16_t* row = reinterpret_cast<uint16_t*>(p.C) + (size_t)m * N;
-#pragma unroll
-      for (int c = 0; c < CW / 8; ++c) {
-        const int n = nbase + 8 * c;
-        if (n >= N) continue;                  // N % 8 == 0: whole vector in range
-        uint4 w;
-        w.x = pack_bf16x2(v[8 * c + 0], v[8 * c + 1]);
-        w.y = pack_bf16x2(v[8 * c + 2], v[8 * c + 3]);
-        w.z = pack_bf16x2(v[8 * c + 4], v[8 * c + 5]);
-        w.w = pack_bf16x2(v[8 * c + 6], v[8 * c + 7]);
-        *reinterpret_cast<uint4*>(row + n) = w;
-      }
-    } else {
-      float* row = reinterpret_cast<float*>(p.C) + (size_t)m * N;
-#pragma unroll
-      for (int c = 0; c < CW / 4; ++c) {
-        const int n = nbase + 4 * c;
-        if (n >= N) continue;
-        *reinterpret_cast<float4*>(row + n) = float4{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
-      }
-    }
+    store_row_span<OUT_BF16, CW>(p.C, size_t(m) * N, nbase, N, v);
   }
 }
 

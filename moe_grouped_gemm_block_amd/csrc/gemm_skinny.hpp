@@ -59,7 +59,7 @@ __device__ __forceinline__ void gemm_skinny_body(const SkinnyJob& p, const int n
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int M = p.M, N = p.N, K = p.K;
-  const int Kb = K / KBLK;
+  const int Kb = (K + KBLK - 1) / KBLK;         // the last K-block may be partial
   const int Nb = (N + KBLK - 1) / KBLK;
 
   typedef const __attribute__((address_space(4))) float cfloat;
@@ -73,8 +73,16 @@ __device__ __forceinline__ void gemm_skinny_body(const SkinnyJob& p, const int n
   // chunk c: LDS rows 8c .. 8c+7; lane L fills row 8c + L/8 slot L%8 with
   // granule (L%8) ^ f(row), f(row) = (L/8) ^ (c & 1)  (see swz16)
   const int lr = lane >> 3;
-  const uint32_t lane_even = uint32_t(lr * K + (((lane & 7) ^ lr) * 16));
-  const uint32_t lane_odd = uint32_t(lr * K + (((lane & 7) ^ lr ^ 1) * 16));
+  const int g_even = ((lane & 7) ^ lr) * 16, g_odd = ((lane & 7) ^ lr ^ 1) * 16;   // source columns
+  const uint32_t lane_even = uint32_t(lr * K + g_even);
+  const uint32_t lane_odd = uint32_t(lr * K + g_odd);
+  // offsets of K-block kb; a granule past K (partial last block) reads as zeros
+  auto off_even = [&](int kb) {
+    return opaque(kb * KBLK + g_even < K ? lane_even + uint32_t(kb * KBLK) : kOutOfRange);
+  };
+  auto off_odd = [&](int kb) {
+    return opaque(kb * KBLK + g_odd < K ? lane_odd + uint32_t(kb * KBLK) : kOutOfRange);
+  };
   const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(
       uint32_t(reinterpret_cast<uintptr_t>(static_cast<void*>(lds))) + uint32_t(wave * WAVE_LDS));
 
@@ -86,8 +94,8 @@ __device__ __forceinline__ void gemm_skinny_body(const SkinnyJob& p, const int n
 
   // wave LDS: [A stage 0][A stage 1][B stage 0][B stage 1][B stage 2] ([sA stage 0][sA stage 1])
   auto issue_a = [&](int kb, int stage) {
-    const uint32_t ev = opaque(lane_even + uint32_t(kb * KBLK));
-    const uint32_t od = opaque(lane_odd + uint32_t(kb * KBLK));
+    const uint32_t ev = off_even(kb);
+    const uint32_t od = off_odd(kb);
     const uint32_t base = lds_wave + uint32_t(stage * A_BYTES);
 #pragma unroll
     for (int c = 0; c < A_CH; ++c)
@@ -96,8 +104,8 @@ __device__ __forceinline__ void gemm_skinny_body(const SkinnyJob& p, const int n
       copy4_to_lds(rS, s_lane + uint32_t(kb * 4), lds_wave + uint32_t(S_OFF + stage * S_BYTES));
   };
   auto issue_b = [&](int kb, int stage) {
-    const uint32_t ev = opaque(lane_even + uint32_t(kb * KBLK));
-    const uint32_t od = opaque(lane_odd + uint32_t(kb * KBLK));
+    const uint32_t ev = off_even(kb);
+    const uint32_t od = off_odd(kb);
     const uint32_t base = lds_wave + uint32_t(2 * A_BYTES + stage * B_BYTES);
 #pragma unroll
     for (int c = 0; c < B_CH; ++c)
@@ -193,7 +201,7 @@ __device__ __forceinline__ void gemm_skinny_body(const SkinnyJob& p, const int n
   for (int c = threadIdx.x; c < RM * CH8; c += 64 * NW) {
     const int m = c / CH8, n8 = (c % CH8) * 8;
     const int n = n0 + n8;
-    if (m >= M || n >= N) continue;             // N % 8 == 0: whole chunk in range
+    if (m >= M || n >= N) continue;
     float v[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) v[t] = 0.f;
@@ -205,18 +213,7 @@ __device__ __forceinline__ void gemm_skinny_body(const SkinnyJob& p, const int n
       v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
       v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
     }
-    if constexpr (OUT_BF16) {
-      uint4 w4;
-      w4.x = pack_bf16x2(v[0], v[1]);
-      w4.y = pack_bf16x2(v[2], v[3]);
-      w4.z = pack_bf16x2(v[4], v[5]);
-      w4.w = pack_bf16x2(v[6], v[7]);
-      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.C) + (size_t)m * N + n) = w4;
-    } else {
-      float* row = reinterpret_cast<float*>(p.C) + (size_t)m * N + n;
-      *reinterpret_cast<float4*>(row) = float4{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<float4*>(row + 4) = float4{v[4], v[5], v[6], v[7]};
-    }
+    store_row_span<OUT_BF16, 8>(p.C, size_t(m) * N, n, N, v);
   }
 }
 
@@ -246,7 +243,7 @@ __device__ __forceinline__ void gemm_skinny_segments(const GemmArgs& p) {
   typedef const __attribute__((address_space(4))) int32_t cint;
   const int lo = min(max(int(((cint*)p.offs)[e]), 0), p.M);
   const int hi = min(max(int(((cint*)p.offs)[e + 1]), lo), p.M);
-  const int N = p.N, K = p.K, Kb = K / KBLK, Nb = (N + KBLK - 1) / KBLK;
+  const int N = p.N, K = p.K, Kb = (K + KBLK - 1) / KBLK, Nb = (N + KBLK - 1) / KBLK;
   const size_t c_row = size_t(N) * (OUT_BF16 ? 2 : 4);
   auto job = [&](int r0, int rows) {
     return SkinnyJob{p.A + size_t(r0) * K, p.sA + size_t(r0) * Kb, p.B + size_t(e) * N * K,

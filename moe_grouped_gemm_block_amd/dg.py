@@ -163,12 +163,12 @@ def _stream(stream):
 def _sa_rows(sA, M, K):
     """Rows per A scale block implied by sA's shape: 128 ([ceil(M/128)][K/128])
     or 1 ([M][K/128]); the first wins where both fit (M <= 1)."""
-    if tuple(sA.shape) == (-(-M // 128), K // 128):
+    if tuple(sA.shape) == (-(-M // 128), -(-K // 128)):
         return 128
-    if tuple(sA.shape) == (M, K // 128):
+    if tuple(sA.shape) == (M, -(-K // 128)):
         return 1
-    raise ValueError(f"sA has shape {tuple(sA.shape)}; expected {(-(-M // 128), K // 128)} "
-                     f"(128 x 128 blocks) or {(M, K // 128)} (1 x 128 blocks)")
+    raise ValueError(f"sA has shape {tuple(sA.shape)}; expected {(-(-M // 128), -(-K // 128))} "
+                     f"(128 x 128 blocks) or {(M, -(-K // 128))} (1 x 128 blocks)")
 
 
 def gemm_fp8_blockscaled(A, sA, B, sB, out_dtype="bf16", C=None, stream=None, a_fmt="e4m3", b_fmt="e4m3"):
@@ -184,7 +184,7 @@ def gemm_fp8_blockscaled(A, sA, B, sB, out_dtype="bf16", C=None, stream=None, a_
         raise ValueError("A and B must share K")
     rows = _sa_rows(sA, M, K)
     _check_f32(sA, "sA", tuple(sA.shape))
-    _check_f32(sB, "sB", (-(-N // 128), K // 128))
+    _check_f32(sB, "sB", (-(-N // 128), -(-K // 128)))
     code = out_code(out_dtype)
     C = _out(C, M, N, code, A)
     fa, fb = fmt_code(a_fmt), fmt_code(b_fmt)
@@ -211,7 +211,7 @@ def grouped_gemm_fp8(A, sA, B, sB, group_offsets, out_dtype="bf16", C=None, stre
         raise ValueError("A and B must share K")
     rows = _sa_rows(sA, M_total, K)
     _check_f32(sA, "sA", tuple(sA.shape))
-    _check_f32(sB, "sB", (G, -(-N // 128), K // 128))
+    _check_f32(sB, "sB", (G, -(-N // 128), -(-K // 128)))
     if (group_offsets.dtype != torch.int32 or not group_offsets.is_cuda
             or tuple(group_offsets.shape) != (G + 1,)):
         raise ValueError("group_offsets must be a device int32 tensor of G + 1 entries")
@@ -242,8 +242,8 @@ def grouped_gemm_fp8_segments(A, sA, B, sB, group_offsets, out_dtype="bf16", C=N
     G, N, K2 = B.shape
     if K != K2:
         raise ValueError("A and B must share K")
-    _check_f32(sA, "sA", (M_total, K // 128))
-    _check_f32(sB, "sB", (G, -(-N // 128), K // 128))
+    _check_f32(sA, "sA", (M_total, -(-K // 128)))
+    _check_f32(sB, "sB", (G, -(-N // 128), -(-K // 128)))
     if (group_offsets.dtype != torch.int32 or not group_offsets.is_cuda
             or tuple(group_offsets.shape) != (G + 1,)):
         raise ValueError("group_offsets must be a device int32 tensor of G + 1 entries")

@@ -112,13 +112,10 @@ def block_scales(x: np.ndarray, fmt: str = "e4m3", rows: int = BLOCK) -> np.ndar
     row block may be partial (R not a multiple of rows).
     """
     R, K = x.shape
-    assert K % BLOCK == 0, "K must be a multiple of 128"
     assert rows in (1, BLOCK)
-    Rb, Kb = -(-R // rows), K // BLOCK
-    pad = Rb * rows - R
-    xa = np.abs(x)
-    if pad:
-        xa = np.concatenate([xa, np.zeros((pad, K), np.float32)], axis=0)
+    Rb, Kb = -(-R // rows), -(-K // BLOCK)       # partial edge blocks in rows and in K
+    xa = np.zeros((Rb * rows, Kb * BLOCK), np.float32)
+    xa[:R, :K] = np.abs(x)
     amax = xa.reshape(Rb, rows, Kb, BLOCK).max(axis=(1, 3)).astype(np.float32)
     s = amax / np.float32(FMT_MAX[fmt])       # fp32 division, RNE
     s = np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
@@ -138,7 +135,7 @@ def quantize(x: np.ndarray, row_chunk: int = 1024, fmt: str = "e4m3",
     for r0 in range(0, R, row_chunk):           # bounded temporaries
         r1 = min(R, r0 + row_chunk)
         srow = np.arange(r0, r1) // rows
-        sexp = np.repeat(s64[srow], BLOCK, axis=1)          # [rows][K]
+        sexp = np.repeat(s64[srow], BLOCK, axis=1)[:, :K]   # [rows][K]
         q[r0:r1] = enc(x[r0:r1].astype(np.float64) / sexp)
     return q, s
 
@@ -221,10 +218,10 @@ def dense_problem(M: int, N: int, K: int, seed: int, out_dtype: str = "bf16",
     if block_log2_range:
         for X in (A, B):
             R = X.shape[0]
-            Rb, Kb = -(-R // BLOCK), K // BLOCK
+            Rb, Kb = -(-R // BLOCK), -(-K // BLOCK)
             u = r_mod.uniform(-block_log2_range, block_log2_range, size=(Rb, Kb))
             mult = np.exp2(u).astype(np.float32)
-            full = np.repeat(np.repeat(mult, BLOCK, axis=0), BLOCK, axis=1)[:R]
+            full = np.repeat(np.repeat(mult, BLOCK, axis=0), BLOCK, axis=1)[:R, :K]
             X *= full
     if outlier_frac:
         hit = r_mod.random((M, K)) < outlier_frac
@@ -260,7 +257,7 @@ def grouped_problem(G: int, N: int, K: int, T: int, seed: int,
     r_act, r_w, _, r_route = streams(seed)
     X = r_act.standard_normal((T, K), dtype=np.float32)
     Bq = np.empty((G, N, K), np.uint8)
-    sB = np.empty((G, -(-N // BLOCK), K // BLOCK), np.float32)
+    sB = np.empty((G, -(-N // BLOCK), -(-K // BLOCK)), np.float32)
     for e in range(G):
         Be = r_w.standard_normal((N, K), dtype=np.float32) * np.float32(b_std)
         Bq[e], sB[e] = quantize(Be)
@@ -316,7 +313,7 @@ def decode_problem(G: int, N: int, K: int, T: int, seed: int, popularity: str = 
     r_act, r_w, _, r_route = streams(seed)
     X = r_act.standard_normal((T, K), dtype=np.float32)
     Bq = np.empty((G, N, K), np.uint8)
-    sB = np.empty((G, -(-N // BLOCK), K // BLOCK), np.float32)
+    sB = np.empty((G, -(-N // BLOCK), -(-K // BLOCK)), np.float32)
     for e in range(G):
         Be = r_w.standard_normal((N, K), dtype=np.float32) * np.float32(b_std)
         Bq[e], sB[e] = quantize(Be)

@@ -113,8 +113,11 @@ def gemm_blockscaled(A: np.ndarray, sA: np.ndarray, B: np.ndarray, sB: np.ndarra
                      sa_rows: int = 128) -> tuple[np.ndarray, np.ndarray]:
     """Dense block-scaled GEMM.
 
-    A: uint8 [M][K] (row-major), sA: fp32 [ceil(M/sa_rows)][K/128]
-    B: uint8 [N][K] (B column-major), sB: fp32 [ceil(N/128)][K/128]
+    A: uint8 [M][K] (row-major), sA: fp32 [ceil(M/sa_rows)][ceil(K/128)]
+    B: uint8 [N][K] (B column-major), sB: fp32 [ceil(N/128)][ceil(K/128)]
+    When K is not a multiple of 128 the last K-block holds the remaining
+    K mod 128 columns and has its own scales, like a partial edge block in M
+    or N (the FP8 kernel write-up, section 6, on the K tail).
     rows / cols: optional index subsets of the output to evaluate.
     a_fmt / b_fmt: "e4m3" (default) or "e5m2" codes.
     sa_rows: rows of A per scale block: 128 (128 x 128 blocks) or 1 (one
@@ -133,11 +136,11 @@ def gemm_blockscaled(A: np.ndarray, sA: np.ndarray, B: np.ndarray, sB: np.ndarra
     """
     M, K = A.shape
     N, K2 = B.shape
-    if K != K2 or K % BLOCK:
-        raise ValueError("A and B must share K, a multiple of 128")
+    if K != K2:
+        raise ValueError("A and B must share K")
     if sa_rows not in (1, BLOCK):
         raise ValueError("sa_rows must be 1 or 128")
-    Kb = K // BLOCK
+    Kb = -(-K // BLOCK)                  # the last K-block may be partial (K tail)
     rows = np.arange(M) if rows is None else np.asarray(rows)
     cols = np.arange(N) if cols is None else np.asarray(cols)
     A64 = decode(A[rows], a_fmt)                              # [m][K]
@@ -145,7 +148,7 @@ def gemm_blockscaled(A: np.ndarray, sA: np.ndarray, B: np.ndarray, sB: np.ndarra
     C = np.zeros((len(rows), len(cols)), np.float64)
     mass = np.zeros_like(C)
     for kb in range(Kb):
-        ks = slice(kb * BLOCK, (kb + 1) * BLOCK)
+        ks = slice(kb * BLOCK, min(K, (kb + 1) * BLOCK))
         a = A64[:, ks]
         b = B64[:, ks]
         partial = a @ b.T                                      # exact for E4M3 x E4M3

@@ -76,8 +76,9 @@ def grouped(A=P, sA=P, B=P, sB=P, C=P, offs=P, G=4, M=512, N=256, K=256, out=1):
     (dict(out=2), INVALID), (dict(out=-1), INVALID),
     (dict(A=P + 8), INVALID), (dict(B=P + 4), INVALID), (dict(C=P + 2), INVALID),
     (dict(sA=P + 2), INVALID), (dict(sB=P + 1), INVALID),
-    (dict(K=200), UNSUP), (dict(K=64), UNSUP), (dict(N=100), UNSUP), (dict(N=12), UNSUP),
+    (dict(K=200), UNSUP), (dict(K=72), UNSUP), (dict(K=1), UNSUP), (dict(K=(1 << 22) + 16), UNSUP),
     (dict(M=0), OK), (dict(N=0), OK), (dict(M=0, A=None, C=None), OK),
+    (dict(M=0, K=144), OK), (dict(M=0, N=13), OK), (dict(N=0, K=16), OK),   # tails are supported
 ])
 def test_dense_validation(L, kw, want):
     assert dense(**kw) == want
@@ -86,7 +87,7 @@ def test_dense_validation(L, kw, want):
 @pytest.mark.parametrize("kw,want", [
     (dict(G=0), INVALID), (dict(G=-3), INVALID), (dict(M=300), INVALID), (dict(M=-128), INVALID),
     (dict(offs=None), INVALID), (dict(offs=P + 2), INVALID), (dict(A=None), INVALID),
-    (dict(out=7), INVALID), (dict(K=100), UNSUP), (dict(N=20), UNSUP),
+    (dict(out=7), INVALID), (dict(K=100), UNSUP), (dict(K=136), UNSUP), (dict(M=0, N=20, K=144), OK),
     (dict(M=0), OK), (dict(N=0), OK),
 ])
 def test_grouped_validation(L, kw, want):
@@ -110,7 +111,7 @@ def grouped_ex(fa=1, fb=0, rows=128, **kw):
 @pytest.mark.parametrize("rows", [128, 1])
 @pytest.mark.parametrize("fa,fb,kw,want", [
     (2, 0, {}, INVALID), (0, -1, {}, INVALID), (1, 1, dict(A=None), INVALID), (1, 0, dict(K=200), UNSUP),
-    (0, 1, dict(out=3), INVALID), (1, 1, dict(M=0), OK), (0, 1, dict(N=12), UNSUP),
+    (0, 1, dict(out=3), INVALID), (1, 1, dict(M=0), OK), (0, 1, dict(K=24), UNSUP),
     (0, 0, dict(sA=P + 2), INVALID), (0, 0, dict(sA=None), INVALID),
 ])
 def test_general_entry_points_validation(L, fa, fb, rows, kw, want):
@@ -139,7 +140,7 @@ def segments(fa=0, fb=0, **kw):
     (2, 0, {}, INVALID), (0, 5, {}, INVALID), (0, 0, dict(G=0), INVALID), (0, 0, dict(G=-1), INVALID),
     (0, 0, dict(offs=None), INVALID), (0, 0, dict(offs=P + 2), INVALID), (0, 0, dict(A=None), INVALID),
     (0, 0, dict(sA=P + 1), INVALID), (1, 1, dict(out=9), INVALID), (0, 0, dict(M=-5), INVALID),
-    (0, 0, dict(K=100), UNSUP), (0, 0, dict(N=20), UNSUP), (0, 0, dict(M=0), OK), (1, 0, dict(N=0), OK),
+    (0, 0, dict(K=100), UNSUP), (0, 0, dict(K=8), UNSUP), (0, 0, dict(M=0), OK), (1, 0, dict(N=0), OK),
 ])
 def test_segments_validation(L, fa, fb, kw, want):
     assert segments(fa, fb, **kw) == want
