@@ -33,6 +33,9 @@ def command(out: str = LIB, extra: list[str] | None = None) -> list[str]:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
             "-Wall", "-Wno-unused-function",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # matrix-core results in ordinary VGPRs: the FP32 rescale reads them
+            # directly instead of copying each one out of an accumulation register
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-I", INCLUDE, "-I", CSRC,
             *[os.path.join(CSRC, s) for s in SOURCES],
             *(extra or []), "-o", out]
