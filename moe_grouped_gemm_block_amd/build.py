@@ -2,24 +2,30 @@
 
     python -m moe_grouped_gemm_block_amd.build
 
-Host and device code are compiled in one hipcc invocation.  Packed FP32
-instructions are disabled for the device code (the host pass warns that it
-does not know the feature; that warning is harmless).
+Each source under csrc/ (the host side plus one translation unit per pair of
+operand formats, see csrc/kernels.hpp) is compiled to an object in parallel,
+then the objects are linked into libdg.so.  Packed FP32 instructions are
+disabled for the device code (the host pass warns that it does not know the
+feature; that warning is harmless).
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdg.so")
-SOURCES = ["dg_api.hip"]
+SOURCES = ["dg_api.hip", "kernels_e4m3.hip", "kernels_e4m3_e5m2.hip", "kernels_e5m2_e4m3.hip",
+           "kernels_e5m2.hip"]
 ARCH = os.environ.get("DG_OFFLOAD_ARCH", "gfx950")
+HARMLESS = "packed-fp32-ops' is not a recognized feature"
 
 
 def hipcc() -> str:
@@ -29,31 +35,43 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC)")
 
 
-def command(out: str = LIB, extra: list[str] | None = None) -> list[str]:
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
+def compile_command(src: str, obj: str) -> list[str]:
+    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c",
             "-Wall", "-Wno-unused-function",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             # matrix-core results in ordinary VGPRs: the FP32 rescale reads them
             # directly instead of copying each one out of an accumulation register
             "-mllvm", "-amdgpu-mfma-vgpr-form=1",
-            "-I", INCLUDE, "-I", CSRC,
-            *[os.path.join(CSRC, s) for s in SOURCES],
-            *(extra or []), "-o", out]
+            "-I", INCLUDE, "-I", CSRC, os.path.join(CSRC, src), "-o", obj]
+
+
+def link_command(objs: list[str], out: str) -> list[str]:
+    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out]
+
+
+def _run(cmd: list[str]) -> str:
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(l for l in res.stderr.splitlines() if HARMLESS not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}\n{errs}")
+    return errs
 
 
 def build(verbose: bool = True) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    errs = "\n".join(l for l in res.stderr.splitlines()
-                     if "packed-fp32-ops' is not a recognized feature" not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
-    if verbose and errs.strip():
-        print(errs, file=sys.stderr)
-    os.replace(tmp, LIB)
+    with tempfile.TemporaryDirectory(prefix="dg_build_") as tmp:
+        objs = [os.path.join(tmp, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [compile_command(s, o) for s, o in zip(SOURCES, objs)]
+        if verbose:
+            for c in cmds:
+                print(" ".join(c), flush=True)
+        jobs = min(len(cmds), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as pool:
+            warnings = list(pool.map(_run, cmds))
+        out_tmp = LIB + ".tmp"
+        warnings.append(_run(link_command(objs, out_tmp)))
+    if verbose and any(w.strip() for w in warnings):
+        print("\n".join(w for w in warnings if w.strip()), file=sys.stderr)
+    os.replace(out_tmp, LIB)
     return LIB
 
 

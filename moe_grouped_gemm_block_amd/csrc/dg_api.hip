@@ -8,6 +8,9 @@
 #include <stdlib.h>
 
 #include "dg.h"
+// this translation unit defines the 1 x 8-wave variant and the quantiser; the
+// GEMM kernels of each operand-format pair are defined in kernels_*.hip
+#define DG_DEFINE_MISC
 #include "gemm_f16mma.hpp"
 #include "gemm_skinny.hpp"
 #include "gemm_wide.hpp"

@@ -44,6 +44,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "kernels.hpp"
 
 namespace dg {
 
@@ -435,25 +436,28 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
 // One named kernel per tile shape, output type and pair of operand formats
 // (suffix _a<A format>b<B format>, 4 = E4M3, 5 = E5M2; E4M3 x E4M3 keeps the
 // plain name); suffix _rs: row-scaled A (1 x 128 scales).
-#define DG_GEMM_KERNEL(NAME, NWM, NWN, BF16, FA, FB, RS)                    \
+#define DG_GEMM_KERNEL_DEF(NAME, NWM, NWN, BF16, FA, FB, RS)                \
   __global__ __launch_bounds__(64 * NWM * NWN, 1) void NAME(GemmArgs p) {   \
     gemm_f16mma_body<NWM, NWN, BF16, FA, FB, RS>(p);                        \
   }
-#define DG_GEMM_SHAPE(SHAPE, NWM, NWN, SFX, FA, FB, RS)                     \
-  DG_GEMM_KERNEL(dg_gemm_##SHAPE##_bf16##SFX, NWM, NWN, true, FA, FB, RS)   \
-  DG_GEMM_KERNEL(dg_gemm_##SHAPE##_f32##SFX, NWM, NWN, false, FA, FB, RS)
-#define DG_GEMM_FORMATS(SFX, FA, FB)                                        \
-  DG_GEMM_SHAPE(128x512, 2, 4, SFX, FA, FB, false)                          \
-  DG_GEMM_SHAPE(128x256, 2, 2, SFX, FA, FB, false)                          \
-  DG_GEMM_SHAPE(128x128, 2, 1, SFX, FA, FB, false)                          \
-  DG_GEMM_SHAPE(128x256, 2, 2, SFX##_rs, FA, FB, true)                      \
-  DG_GEMM_SHAPE(128x128, 2, 1, SFX##_rs, FA, FB, true)
-DG_GEMM_FORMATS(, FMT_E4M3, FMT_E4M3)
-DG_GEMM_FORMATS(_a5b5, FMT_E5M2, FMT_E5M2)
-DG_GEMM_FORMATS(_a4b5, FMT_E4M3, FMT_E5M2)
-DG_GEMM_FORMATS(_a5b4, FMT_E5M2, FMT_E4M3)
+#define DG_GEMM_KERNEL_DECL(NAME, NWM, NWN, BF16, FA, FB, RS) \
+  __global__ __launch_bounds__(64 * NWM * NWN, 1) void NAME(GemmArgs p);
+#define DG_GEMM_SHAPE(K, SHAPE, NWM, NWN, SFX, FA, FB, RS)                  \
+  K(dg_gemm_##SHAPE##_bf16##SFX, NWM, NWN, true, FA, FB, RS)                \
+  K(dg_gemm_##SHAPE##_f32##SFX, NWM, NWN, false, FA, FB, RS)
+#define DG_GEMM_FORMATS(K, SFX, FA, FB)                                     \
+  DG_GEMM_SHAPE(K, 128x512, 2, 4, SFX, FA, FB, false)                       \
+  DG_GEMM_SHAPE(K, 128x256, 2, 2, SFX, FA, FB, false)                       \
+  DG_GEMM_SHAPE(K, 128x128, 2, 1, SFX, FA, FB, false)                       \
+  DG_GEMM_SHAPE(K, 128x256, 2, 2, SFX##_rs, FA, FB, true)                   \
+  DG_GEMM_SHAPE(K, 128x128, 2, 1, SFX##_rs, FA, FB, true)
+DG_GEMM_FORMATS(DG_KERNEL(DG_GEMM_KERNEL, FMT_44), , FMT_E4M3, FMT_E4M3)
+DG_GEMM_FORMATS(DG_KERNEL(DG_GEMM_KERNEL, FMT_55), _a5b5, FMT_E5M2, FMT_E5M2)
+DG_GEMM_FORMATS(DG_KERNEL(DG_GEMM_KERNEL, FMT_45), _a4b5, FMT_E4M3, FMT_E5M2)
+DG_GEMM_FORMATS(DG_KERNEL(DG_GEMM_KERNEL, FMT_54), _a5b4, FMT_E5M2, FMT_E4M3)
 #undef DG_GEMM_FORMATS
 #undef DG_GEMM_SHAPE
-#undef DG_GEMM_KERNEL
+#undef DG_GEMM_KERNEL_DECL
+#undef DG_GEMM_KERNEL_DEF
 
 }  // namespace dg

@@ -263,39 +263,39 @@ __device__ __forceinline__ void gemm_skinny_segments(const GemmArgs& p) {
   }
 }
 
-#define DG_SKINNY_KERNEL(NAME, MI, NI, BF16, FA, FB, RS) \
+#define DG_SKINNY_KERNEL_DEF(NAME, MI, NI, BF16, FA, FB, RS) \
   __global__ __launch_bounds__(256, 1) void NAME(GemmArgs p) { gemm_skinny_dense<MI, NI, BF16, FA, FB, RS>(p); }
-#define DG_SKINNY_SHAPE(ROWS, COLS, MI, NI, SFX, FA, FB, RS)                                \
-  DG_SKINNY_KERNEL(dg_skinny_m##ROWS##_n##COLS##_bf16##SFX, MI, NI, true, FA, FB, RS)       \
-  DG_SKINNY_KERNEL(dg_skinny_m##ROWS##_n##COLS##_f32##SFX, MI, NI, false, FA, FB, RS)
-#define DG_SKINNY_ROWS(SFX, FA, FB, RS)                                                     \
-  DG_SKINNY_SHAPE(64, 48, 4, 3, SFX, FA, FB, RS) DG_SKINNY_SHAPE(64, 16, 4, 1, SFX, FA, FB, RS) \
-  DG_SKINNY_SHAPE(32, 48, 2, 3, SFX, FA, FB, RS) DG_SKINNY_SHAPE(32, 16, 2, 1, SFX, FA, FB, RS) \
-  DG_SKINNY_SHAPE(16, 48, 1, 3, SFX, FA, FB, RS) DG_SKINNY_SHAPE(16, 16, 1, 1, SFX, FA, FB, RS)
-#define DG_SKINNY_FORMATS(SFX, FA, FB)   \
-  DG_SKINNY_ROWS(SFX, FA, FB, false)     \
-  DG_SKINNY_ROWS(SFX##_rs, FA, FB, true)
-DG_SKINNY_FORMATS(, FMT_E4M3, FMT_E4M3)
-DG_SKINNY_FORMATS(_a5b5, FMT_E5M2, FMT_E5M2)
-DG_SKINNY_FORMATS(_a4b5, FMT_E4M3, FMT_E5M2)
-DG_SKINNY_FORMATS(_a5b4, FMT_E5M2, FMT_E4M3)
-#undef DG_SKINNY_FORMATS
-
-#define DG_SEG_KERNEL(NAME, NI, BF16, FA, FB) \
+#define DG_SKINNY_KERNEL_DECL(NAME, MI, NI, BF16, FA, FB, RS) \
+  __global__ __launch_bounds__(256, 1) void NAME(GemmArgs p);
+#define DG_SKINNY_SHAPE(K, ROWS, COLS, MI, NI, SFX, FA, FB, RS)               \
+  K(dg_skinny_m##ROWS##_n##COLS##_bf16##SFX, MI, NI, true, FA, FB, RS)        \
+  K(dg_skinny_m##ROWS##_n##COLS##_f32##SFX, MI, NI, false, FA, FB, RS)
+#define DG_SKINNY_ROWS(K, SFX, FA, FB, RS)                                                          \
+  DG_SKINNY_SHAPE(K, 64, 48, 4, 3, SFX, FA, FB, RS) DG_SKINNY_SHAPE(K, 64, 16, 4, 1, SFX, FA, FB, RS) \
+  DG_SKINNY_SHAPE(K, 32, 48, 2, 3, SFX, FA, FB, RS) DG_SKINNY_SHAPE(K, 32, 16, 2, 1, SFX, FA, FB, RS) \
+  DG_SKINNY_SHAPE(K, 16, 48, 1, 3, SFX, FA, FB, RS) DG_SKINNY_SHAPE(K, 16, 16, 1, 1, SFX, FA, FB, RS)
+#define DG_SEG_KERNEL_DEF(NAME, NI, BF16, FA, FB) \
   __global__ __launch_bounds__(256, 1) void NAME(GemmArgs p) { gemm_skinny_segments<NI, BF16, FA, FB>(p); }
-#define DG_SEG_SHAPE(COLS, NI, SFX, FA, FB)                              \
-  DG_SEG_KERNEL(dg_segments_n##COLS##_bf16##SFX, NI, true, FA, FB)       \
-  DG_SEG_KERNEL(dg_segments_n##COLS##_f32##SFX, NI, false, FA, FB)
-#define DG_SEG_FORMATS(SFX, FA, FB) DG_SEG_SHAPE(48, 3, SFX, FA, FB) DG_SEG_SHAPE(16, 1, SFX, FA, FB)
-DG_SEG_FORMATS(, FMT_E4M3, FMT_E4M3)
-DG_SEG_FORMATS(_a5b5, FMT_E5M2, FMT_E5M2)
-DG_SEG_FORMATS(_a4b5, FMT_E4M3, FMT_E5M2)
-DG_SEG_FORMATS(_a5b4, FMT_E5M2, FMT_E4M3)
-#undef DG_SEG_FORMATS
+#define DG_SEG_KERNEL_DECL(NAME, NI, BF16, FA, FB) __global__ __launch_bounds__(256, 1) void NAME(GemmArgs p);
+#define DG_SEG_SHAPE(K, COLS, NI, SFX, FA, FB)                \
+  K(dg_segments_n##COLS##_bf16##SFX, NI, true, FA, FB)        \
+  K(dg_segments_n##COLS##_f32##SFX, NI, false, FA, FB)
+#define DG_FEW_ROWS_FORMATS(GROUP, SFX, FA, FB)                                \
+  DG_SKINNY_ROWS(DG_KERNEL(DG_SKINNY_KERNEL, GROUP), SFX, FA, FB, false)      \
+  DG_SKINNY_ROWS(DG_KERNEL(DG_SKINNY_KERNEL, GROUP), SFX##_rs, FA, FB, true)  \
+  DG_SEG_SHAPE(DG_KERNEL(DG_SEG_KERNEL, GROUP), 48, 3, SFX, FA, FB)           \
+  DG_SEG_SHAPE(DG_KERNEL(DG_SEG_KERNEL, GROUP), 16, 1, SFX, FA, FB)
+DG_FEW_ROWS_FORMATS(FMT_44, , FMT_E4M3, FMT_E4M3)
+DG_FEW_ROWS_FORMATS(FMT_55, _a5b5, FMT_E5M2, FMT_E5M2)
+DG_FEW_ROWS_FORMATS(FMT_45, _a4b5, FMT_E4M3, FMT_E5M2)
+DG_FEW_ROWS_FORMATS(FMT_54, _a5b4, FMT_E5M2, FMT_E4M3)
+#undef DG_FEW_ROWS_FORMATS
 #undef DG_SEG_SHAPE
-#undef DG_SEG_KERNEL
+#undef DG_SEG_KERNEL_DECL
+#undef DG_SEG_KERNEL_DEF
 #undef DG_SKINNY_ROWS
 #undef DG_SKINNY_SHAPE
-#undef DG_SKINNY_KERNEL
+#undef DG_SKINNY_KERNEL_DECL
+#undef DG_SKINNY_KERNEL_DEF
 
 }  // namespace dg

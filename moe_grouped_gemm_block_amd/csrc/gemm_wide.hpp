@@ -310,10 +310,12 @@ __device__ __forceinline__ void gemm_wide_body(const GemmArgs& p) {
   }
 }
 
-#define DG_WIDE_KERNEL(NAME, BF16) \
+#define DG_WIDE_KERNEL_DEF(NAME, BF16) \
   __global__ __launch_bounds__(512, 1) void NAME(GemmArgs p) { gemm_wide_body<BF16>(p); }
-DG_WIDE_KERNEL(dg_gemm_wide_128x512_bf16, true)
-DG_WIDE_KERNEL(dg_gemm_wide_128x512_f32, false)
-#undef DG_WIDE_KERNEL
+#define DG_WIDE_KERNEL_DECL(NAME, BF16) __global__ __launch_bounds__(512, 1) void NAME(GemmArgs p);
+DG_KERNEL(DG_WIDE_KERNEL, MISC)(dg_gemm_wide_128x512_bf16, true)
+DG_KERNEL(DG_WIDE_KERNEL, MISC)(dg_gemm_wide_128x512_f32, false)
+#undef DG_WIDE_KERNEL_DECL
+#undef DG_WIDE_KERNEL_DEF
 
 }  // namespace dg

@@ -1,0 +1,5 @@
+// Definitions of the GEMM kernels with E5M2 A and E5M2 B operands (tiled, few-rows and
+// packed-segment kernels); the other translation units only declare them.
+#define DG_DEFINE_FMT_55
+#include "gemm_f16mma.hpp"
+#include "gemm_skinny.hpp"

@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.hpp"
+
 namespace dg {
 
 struct QuantArgs {
@@ -211,12 +213,14 @@ __device__ __forceinline__ void quant1_body(const QuantArgs& p) {
   }
 }
 
-#define DG_QUANT_KERNEL(NAME, BODY, BF16) \
+#define DG_QUANT_KERNEL_DEF(NAME, BODY, BF16) \
   __global__ __launch_bounds__(256) void NAME(QuantArgs p) { BODY<BF16>(p); }
-DG_QUANT_KERNEL(dg_quant_128x128_bf16, quant128_body, true)
-DG_QUANT_KERNEL(dg_quant_128x128_f32, quant128_body, false)
-DG_QUANT_KERNEL(dg_quant_1x128_bf16, quant1_body, true)
-DG_QUANT_KERNEL(dg_quant_1x128_f32, quant1_body, false)
-#undef DG_QUANT_KERNEL
+#define DG_QUANT_KERNEL_DECL(NAME, BODY, BF16) __global__ __launch_bounds__(256) void NAME(QuantArgs p);
+DG_KERNEL(DG_QUANT_KERNEL, MISC)(dg_quant_128x128_bf16, quant128_body, true)
+DG_KERNEL(DG_QUANT_KERNEL, MISC)(dg_quant_128x128_f32, quant128_body, false)
+DG_KERNEL(DG_QUANT_KERNEL, MISC)(dg_quant_1x128_bf16, quant1_body, true)
+DG_KERNEL(DG_QUANT_KERNEL, MISC)(dg_quant_1x128_f32, quant1_body, false)
+#undef DG_QUANT_KERNEL_DECL
+#undef DG_QUANT_KERNEL_DEF
 
 }  // namespace dg
