@@ -91,14 +91,15 @@ typedef void (*kfn)(dg::GemmArgs);
 
 // Kernels of one pair of operand formats; combo = 2 * a_fmt + b_fmt.  The
 // *rs kernels take one A scale per row (1 x 128 blocks).
-struct TiledSet { kfn k512[2], k256[2], k128[2], k256rs[2], k128rs[2]; };   // [f32, bf16]
+struct TiledSet { kfn k512[2], k256[2], k128[2]; };   // [f32, bf16]
 #define DG_TILED_SET(SFX)                                                   \
   {{dg::dg_gemm_128x512_f32##SFX, dg::dg_gemm_128x512_bf16##SFX},           \
    {dg::dg_gemm_128x256_f32##SFX, dg::dg_gemm_128x256_bf16##SFX},           \
-   {dg::dg_gemm_128x128_f32##SFX, dg::dg_gemm_128x128_bf16##SFX},           \
-   {dg::dg_gemm_128x256_f32##SFX##_rs, dg::dg_gemm_128x256_bf16##SFX##_rs}, \
-   {dg::dg_gemm_128x128_f32##SFX##_rs, dg::dg_gemm_128x128_bf16##SFX##_rs}}
-const TiledSet kTiled[4] = {DG_TILED_SET(), DG_TILED_SET(_a4b5), DG_TILED_SET(_a5b4), DG_TILED_SET(_a5b5)};
+   {dg::dg_gemm_128x128_f32##SFX, dg::dg_gemm_128x128_bf16##SFX}}
+// [A scales per 128 x 128 block / per row][combo]
+const TiledSet kTiled[2][4] = {
+    {DG_TILED_SET(), DG_TILED_SET(_a4b5), DG_TILED_SET(_a5b4), DG_TILED_SET(_a5b5)},
+    {DG_TILED_SET(_rs), DG_TILED_SET(_a4b5_rs), DG_TILED_SET(_a5b4_rs), DG_TILED_SET(_a5b5_rs)}};
 #undef DG_TILED_SET
 
 // [A scales per block / per row][rows 16/32/64][NI 1/3][f32/bf16]
@@ -156,23 +157,16 @@ int launch_segments(dg::GemmArgs a, int out_dtype, int combo, hipStream_t stream
 
 int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, int row_sa, hipStream_t stream) {
   const int combo = 2 * a_fmt + b_fmt;
-  const TiledSet& ks = kTiled[combo];
+  const TiledSet& ks = kTiled[row_sa][combo];
   if (a.offs == nullptr && a.M <= 64 && forced_tile() == 0)
     return launch_skinny(a, out_dtype, combo, row_sa, stream);
-  if (row_sa) {
-    // Per-row A scales need a small LDS stage next to the A and B stages,
-    // which the 160 KB of the 128 x 512 tile leave no room for.
-    if (forced_tile() == 128 || a.N <= 128)
-      return launch_tiles(a, 128, 128, ks.k128rs[1], ks.k128rs[0], out_dtype, stream);
-    return launch_tiles(a, 256, 256, ks.k256rs[1], ks.k256rs[0], out_dtype, stream);
-  }
   const int64_t m_tiles = (int64_t(a.M) + 127) / 128;
   const int64_t wide = m_tiles * ((int64_t(a.N) + 511) / 512);
   bool use512 = a.N > 256 && wide >= kCUs / 2;
   if (forced_tile() == 512) use512 = true;
   if (forced_tile() == 256) use512 = false;
   // the 1 x 8 variant exists for E4M3 x E4M3 without K or N tails
-  if (forced_tile() == 1512 && combo == 0 && a.K % dg::KBLK == 0 && a.N % 8 == 0)
+  if (forced_tile() == 1512 && combo == 0 && !row_sa && a.K % dg::KBLK == 0 && a.N % 8 == 0)
     return launch_tiles(a, 512, 512, dg::dg_gemm_wide_128x512_bf16, dg::dg_gemm_wide_128x512_f32, out_dtype,
                         stream);
   if (use512 && forced_tile() == 0 && tail_tile() != 0) {

@@ -195,8 +195,11 @@ __device__ __forceinline__ void tile_of(int bid, int m_tiles, int n_tiles, int& 
   tn = r / gsize;
 }
 
-// ROW_SA: sA holds one scale per row and K-block ([rows][K/128], the 1 x 128
-// per-token granularity) instead of one per 128 x 128 block.
+// ROW_SA: sA holds one scale per row and K-block ([rows][Kb], the 1 x 128
+// per-token granularity) instead of one per 128 x 128 block.  Each lane then
+// loads the scales of its four rows one K-block ahead with ordinary vector
+// loads: the loop drains every copy (vmcnt(0)) at the end of each K-block
+// anyway, so waiting for these loads costs nothing, and no LDS is needed.
 template <int NWM, int NWN, bool OUT_BF16, int FA = FMT_E4M3, int FB = FMT_E4M3, bool ROW_SA = false>
 __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   constexpr int WM = 64, WN = 128;             // wave sub-tile
@@ -207,10 +210,8 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   constexpr int A_CH = BM / 8 / NW, B_CH = BN / 8 / NW;   // 1 KB copy chunks per wave
   static_assert(A_CH * 8 * NW == BM && B_CH * 8 * NW == BN, "chunking");
   static_assert(NW % 2 == 0, "chunk parity per wave assumes an even wave count");
-  constexpr int SA_BYTES = ROW_SA ? BM * 4 : 0;   // one K-block's row scales
-  static_assert(!ROW_SA || NW >= BM / 64, "row scales are copied by the first BM/64 waves");
-  // LDS: [A stage 0][A stage 1][B stage 0][B stage 1] ([sA stage 0][sA stage 1])
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (A_BYTES + B_BYTES + SA_BYTES)];
+  // LDS: [A stage 0][A stage 1][B stage 0][B stage 1]
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (A_BYTES + B_BYTES)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -258,20 +259,7 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   // LDS byte address of the buffer (wave-uniform)
   const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
       uint32_t(reinterpret_cast<uintptr_t>(static_cast<void*>(lds))));
-  // row scales of the tile: wave w < BM/64 copies rows 64 w .. 64 w + 63,
-  // 4 bytes per lane; rows past M read as zeros
-  i32x4 rS{};
-  uint32_t s_lane = 0;
-  if constexpr (ROW_SA) {
-    rS = make_rsrc(p.sA + (size_t)m0 * Kb, uint32_t(min(M - m0, BM)) * uint32_t(Kb) * 4u);
-    s_lane = uint32_t((wave * 64 + lane) * Kb * 4);
-  }
   auto issue_copies = [&](int kb, int stage) {
-    if constexpr (ROW_SA) {
-      if (wave < BM / 64)
-        copy4_to_lds(rS, s_lane + uint32_t(kb * 4),
-                     lds_addr + uint32_t(2 * (A_BYTES + B_BYTES) + stage * SA_BYTES + wave * 256));
-    }
     // a granule past K (partial last K-block) reads as zeros: its offset is
     // pushed past the buffer end (all offsets stay below 2^32)
     const bool k_in = kb * KBLK + gsl < K;
@@ -312,6 +300,22 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
     __syncthreads();
   }
 
+  // ROW_SA: lane L loads the scale of row wm + L (the wave's 64 rows, one
+  // register), through a buffer that ends at the matrix edge (rows past M
+  // read as 0; their output is never stored); each lane then fetches the
+  // scales of its rows wm + 16 mi + r16 from lanes 16 mi + r16
+  const __amdgpu_buffer_rsrc_t rS = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(p.sA) + (size_t)m0 * Kb, 0,
+      ROW_SA ? int(uint32_t(min(M - m0, BM)) * uint32_t(Kb) * 4u) : 0, 0x00020000);
+  const uint32_t s_off = uint32_t((wm + lane) * Kb * 4);
+  float sa_lane = 0.f;                         // scale of row wm + lane, next K-block
+  auto load_row_scales = [&](int kb) {
+    sa_lane = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rS, int(s_off + uint32_t(kb * 4)), 0, 0));
+  };
+  if constexpr (ROW_SA) {
+    if (Kb > 0) load_row_scales(0);
+  }
+
   float sa_next = Kb > 0 && !ROW_SA ? float(sAr[0]) : 1.f, sb_next = Kb > 0 ? sBr[0] : 0.f;
   for (int kb = 0; kb < Kb; ++kb) {
     const int stage = kb & 1;
@@ -320,12 +324,19 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) s_m[mi] = s;
     if constexpr (ROW_SA) {
-      const float* ls = reinterpret_cast<const float*>(lds + 2 * (A_BYTES + B_BYTES) + stage * SA_BYTES);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) s_m[mi] = ls[wm + 16 * mi + r16] * sb_next;
+      for (int mi = 0; mi < MI; ++mi) {
+        s_m[mi] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (16 * mi + r16),
+                                                                         __builtin_bit_cast(int, sa_lane))) *
+                  sb_next;
+        // consumed before the next copies are issued, so that the wait for
+        // these loads cannot fall after (and drain) those copies
+        asm volatile("" : "+v"(s_m[mi]));
+      }
     }
     if (kb + 1 < Kb) {
-      if constexpr (!ROW_SA) sa_next = sAr[kb + 1];   // prefetched one K-block ahead
+      if constexpr (ROW_SA) load_row_scales(kb + 1);   // prefetched one K-block ahead
+      else sa_next = sAr[kb + 1];
       sb_next = sBr[kb + 1];
       issue_copies(kb + 1, stage ^ 1);
     }
@@ -449,6 +460,7 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   DG_GEMM_SHAPE(K, 128x512, 2, 4, SFX, FA, FB, false)                       \
   DG_GEMM_SHAPE(K, 128x256, 2, 2, SFX, FA, FB, false)                       \
   DG_GEMM_SHAPE(K, 128x128, 2, 1, SFX, FA, FB, false)                       \
+  DG_GEMM_SHAPE(K, 128x512, 2, 4, SFX##_rs, FA, FB, true)                   \
   DG_GEMM_SHAPE(K, 128x256, 2, 2, SFX##_rs, FA, FB, true)                   \
   DG_GEMM_SHAPE(K, 128x128, 2, 1, SFX##_rs, FA, FB, true)
 DG_GEMM_FORMATS(DG_KERNEL(DG_GEMM_KERNEL, FMT_44), , FMT_E4M3, FMT_E4M3)
