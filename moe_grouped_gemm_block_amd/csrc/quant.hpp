@@ -18,13 +18,12 @@
 // included) and each |x| to a = |x| 2^-e (exact: a <= |x| / s * s_n < 448 can
 // not overflow, and an a that underflows is far below the first E4M3
 // midpoint).  An approximate quotient y = a * fp32(1 / s_n), within a few
-// ulp of a / s_n, only picks the two E4M3 grid values lo < hi around it; the
-// nearest grid value of the exact quotient is always one of them, because
-// grid steps are at least 2^-3 of the value.  The choice is then exact: the
-// midpoint m = (lo + hi) / 2 has at most 5 significant bits, so
-// fma(m, s_n, -a) has the sign of m s_n - a, i.e. of m - |x| / s, and is zero
-// only at an exact tie, which goes to the even grid index.  Binade edges need
-// no special case: a grid index of 16 carries into the exponent field.
+// ulp of a / s_n, only picks the two E4M3 grid values lo < hi around it (lo
+// read off y's bits); the nearest grid value of the exact quotient is always
+// one of them, because grid steps are at least 2^-4 of the value.  The
+// choice is then exact: the midpoint m = (lo + hi) / 2 has at most 5
+// significant bits, so fma(m, s_n, -a) has the sign of m s_n - a, i.e. of
+// m - |x| / s, and is zero only at an exact tie, which goes to the even code.
 // The scale fp32(double(amax) / 448) equals the IEEE FP32 quotient (double
 // rounding through 53 bits is innocuous for one division of 24-bit numbers).
 //
@@ -63,23 +62,28 @@ __device__ __forceinline__ ScaleNorm scale_norm(float s) {
 
 // E4M3FN code of x / s: nearest value, ties to even, capped at 448, sign of x.
 __device__ __forceinline__ uint32_t e4m3_code(float x, const ScaleNorm& n) {
-  const uint32_t sign = (__float_as_uint(x) >> 31) << 7;
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
   const float a = __builtin_ldexpf(__builtin_fabsf(x), -n.e);
   const float y = a * n.inv_n;                            // ~ |x| / s
-  // grid around y: below 2^-6 steps of 2^-9 (codes 0 .. 8); in [2^E, 2^(E+1))
-  // steps of 2^(E-3) (codes (E+7) << 3 | 0 .. 7); step index k of lo
-  const int E = max(int((__float_as_uint(y) >> 23) & 0xFF) - 127, -6);
-  const float step = __uint_as_float(uint32_t(E - 3 + 127) << 23);        // 2^(E-3)
-  const float k = __builtin_floorf(__builtin_ldexpf(y, 3 - E));          // exact scaling
-  const float mid = (k + 0.5f) * step;                                    // exact (5 bits)
-  const float r = __builtin_fmaf(mid, n.s_n, -a);                         // sign of mid - |x|/s
-  const uint32_t ki = uint32_t(k);
-  const uint32_t kk = ki + uint32_t(r < 0.f || (r == 0.f && (ki & 1u)));  // nearest, ties to even
-  // code ((E + 7) << 3) + kk - 8: also right below 2^-6 (E clamped to -6,
-  // kk = 0 .. 8 are the subnormal codes and 2^-6), and kk = 16 carries into
-  // the next binade
-  const uint32_t code = (uint32_t(E + 7) << 3) + kk - 8u;
-  return sign | min(code, 0x7Eu);
+  // Grid point at or below y, read off the FP32 bits: in [2^E, 2^(E+1))
+  // (E >= -6) the E4M3 code is ((E + 7) << 3) | m for the top three mantissa
+  // bits m, i.e. (bits >> 20) - (120 << 3).  Below 2^-6 the grid (codes
+  // 0 .. 8, spacing 2^-9) is that of [2^-6, 2^-5) shifted down by 2^-6, so y
+  // is moved there first; that addition may round, but only across a grid
+  // point that y is within an ulp of, where the decision below still picks
+  // the nearest value.
+  const bool sub = y < 0x1p-6f;
+  const float c = sub ? 0x1p-6f : 0.f;
+  const uint32_t tb = __float_as_uint(y + c);
+  const uint32_t lo = (tb >> 20) - (sub ? 968u : 960u);
+  // midpoint above that grid point: one more mantissa bit (exact, 5
+  // significant bits), moved back by c (exact)
+  const float mid = __uint_as_float((tb & 0xFFF00000u) | 0x00080000u) - c;
+  const float r = __builtin_fmaf(mid, n.s_n, -a);         // sign of mid - |x|/s, exact
+  const uint32_t up = uint32_t(r < 0.f || (r == 0.f && (lo & 1u)));   // nearest, ties to even
+  // a code past 0x7E (above 448, or the carry into the next binade at the
+  // top) saturates
+  return sign | min(lo + up, 0x7Eu);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
