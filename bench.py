@@ -67,8 +67,11 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources and of the build script (its compiler flags shape the code)."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "moe_grouped_gemm_block_amd", "csrc", "*"))):
+    files = sorted(glob.glob(os.path.join(ROOT, "moe_grouped_gemm_block_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "moe_grouped_gemm_block_amd", "build.py"))
+    for f in files:
         h.update(os.path.basename(f).encode())
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
