@@ -49,9 +49,10 @@ int check_common(const void* A, const float* sA, const void* B, const float* sB,
 // LDS); the 128 x 256 tile runs 4 waves, serves narrow problems and finishes
 // the last partial round of a large problem (see launch()); the 128 x 128
 // tile (2 waves, 64 KB of LDS) is the alternative for that last round.
-// DG_FORCE_TILE=512 or 256 overrides the choice, 1512 selects the 1 x 8
-// wave arrangement; DG_TAIL_TILE=0 / 128 / 256 switches off or sets the
-// tile of the last partial round (tuning aids).
+// DG_FORCE_TILE=512, 256 or 128 uses that tile for every problem (few rows
+// included), 1512 selects the 1 x 8 wave arrangement where it applies;
+// DG_TAIL_TILE=0 / 128 / 256 switches off or sets the tile of the last
+// partial round (tuning aids).
 constexpr int kCUs = 256;
 
 int forced_tile() {
@@ -169,6 +170,7 @@ int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, int row_s
   if (forced_tile() == 1512 && combo == 0 && !row_sa && a.K % dg::KBLK == 0 && a.N % 8 == 0)
     return launch_tiles(a, 512, 512, dg::dg_gemm_wide_128x512_bf16, dg::dg_gemm_wide_128x512_f32, out_dtype,
                         stream);
+  if (forced_tile() == 128) return launch_tiles(a, 128, 128, ks.k128[1], ks.k128[0], out_dtype, stream);
   if (use512 && forced_tile() == 0 && tail_tile() != 0) {
     // A 128 x 512 tile takes about as long whether 1 or all 256 CUs are busy,
     // so a last round that is only partly filled costs almost a full round.

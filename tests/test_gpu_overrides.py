@@ -1,0 +1,29 @@
+"""The tile-choice overrides (DG_FORCE_TILE: 1512 = the 1 x 8-wave variant,
+512 / 256 / 128 = one tile shape for every problem; DG_TAIL_TILE: 0 = no
+separate last round, 128 = 128 x 128 tiles for it) give results inside the
+parity bound.  The library reads them once per process, so every setting
+runs tests/override_child.py in a child process.  Needs a GPU."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.mark.parametrize("env", [{"DG_FORCE_TILE": "1512"}, {"DG_FORCE_TILE": "512"},
+                                 {"DG_FORCE_TILE": "256"}, {"DG_FORCE_TILE": "128"},
+                                 {"DG_TAIL_TILE": "0"}, {"DG_TAIL_TILE": "128"}],
+                         ids=lambda e: "_".join(f"{k}={v}" for k, v in e.items()))
+def test_tile_override(env):
+    full = dict(os.environ)
+    full.pop("DG_FORCE_TILE", None)
+    full.pop("DG_TAIL_TILE", None)
+    full.update(env)
+    r = subprocess.run([sys.executable, os.path.join(HERE, "override_child.py")], env=full,
+                       capture_output=True, text=True, timeout=240)
+    print(r.stdout, file=sys.stderr)
+    assert r.returncode == 0, r.stdout + r.stderr[-2000:]
