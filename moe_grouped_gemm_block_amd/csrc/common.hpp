@@ -33,17 +33,16 @@ __device__ __forceinline__ v4f mfma16_fp8_acc(const v8i& a, const v8i& b, const 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// FP32 -> BF16, round to nearest even (finite inputs; NaN stays NaN).
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// FP32 -> BF16, round to nearest even (NaN stays NaN): gfx950 converts two
+// values per instruction (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
 }
+
+__device__ __forceinline__ uint32_t bf16_bits(float f) { return pack_bf16x2(f, 0.f) & 0xFFFFu; }
 
 // Buffer offset that lies past any buffer's end (num_records <= 2^31 here):
 // a load from it returns zeros.  Row offsets below 2^31 can be added to it
