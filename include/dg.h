@@ -1,6 +1,9 @@
 /*
- * dg.h -- C ABI of libdg.so: FP8 (E4M3) GEMM with 128x128 block scales on
- * AMD Instinct MI355X (gfx950), dense and MoE-grouped.
+ * dg.h -- C ABI of libdg.so: block-scaled FP8 GEMM on AMD Instinct MI355X
+ * (gfx950), dense and MoE-grouped, and the FP8 quantisation of activations
+ * that produces its A operand.  The base calls take E4M3 operands with
+ * 128x128 block scales; the _ex calls add E5M2 operands and per-token (1 x 128)
+ * A scales, dg_grouped_gemm_fp8_segments serves decode-time MoE.
  *
  * The operation (DeepGEMM FP8-for-MoE page, 2kiu.com/news/5461879,
  * section 2.1 "block-wise scaling"; FP32 accumulation, section 3.3):
@@ -52,6 +55,10 @@
  *     writes zeros.
  *   - A failed kernel launch returns DG_ERR_LAUNCH.  Faults inside a kernel
  *     surface at the caller's next synchronisation, as for any HIP kernel.
+ *   - Every call only enqueues kernels (no allocation, no memset, no host
+ *     synchronisation), so it may be captured into a HIP graph and replayed.
+ *   - Results are bitwise repeatable: no atomics, and every output element
+ *     is summed in a fixed order.
  *   - Out of scope: alpha / beta (C is overwritten, alpha = 1, beta = 0),
  *     transposed layouts other than the above, other element types.
  */
