@@ -126,3 +126,26 @@ def test_quantized_operand_feeds_the_gemm():
     Cr, mass = oracle.gemm_blockscaled(qao, sao, qbo, sbo)
     err = np.abs(C.cpu().numpy().astype(np.float64) - Cr)
     assert np.all(err <= oracle.tolerance(Cr, mass, "f32"))
+
+
+@pytest.mark.parametrize("R", [128, 1])
+def test_quantize_writes_nothing_outside_q_and_s(R):
+    """Q and S are views into larger buffers filled with a marker: the bytes
+    before and after them are untouched (ragged M, several K-blocks)."""
+    log(f"quantize guard bands R={R}")
+    rng = np.random.default_rng(9)
+    M, K = 131, 384
+    x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    G = 256
+    qbuf = torch.full((M * K + 2 * G,), 0x5A, dtype=torch.uint8, device=DEV)
+    ns = -(-M // R) * (K // 128)
+    sbuf = torch.full((ns + 2 * 64,), 7.0, dtype=torch.float32, device=DEV)
+    Q = qbuf[G:G + M * K].view(M, K)
+    S = sbuf[64:64 + ns].view(-(-M // R), K // 128)
+    dg.quantize_fp8_blockscaled(x, R, Q=Q, S=S)
+    torch.cuda.synchronize()
+    qb, sb = qbuf.cpu().numpy(), sbuf.cpu().numpy()
+    assert np.all(qb[:G] == 0x5A) and np.all(qb[G + M * K:] == 0x5A)
+    assert np.all(sb[:64] == 7.0) and np.all(sb[64 + ns:] == 7.0)
+    qo, so = oracle.quantize_blockscaled(x.float().cpu().numpy(), R)
+    assert np.array_equal(Q.cpu().numpy(), qo) and np.array_equal(S.cpu().numpy(), so)
