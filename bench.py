@@ -28,6 +28,8 @@ Workloads (seeded, synthetic; see inputs.make_config):
 
 --op quantize times the activation quantisation that produces A instead
 (4096 x 4096 BF16 in, E4M3 codes and FP32 block scales out; HBM-bound).
+--op torch-matmul times the vendor library's plain BF16 (or FP16) GEMM,
+torch.matmul on 4096^3, as a reference point for the matrix cores' rate.
 """
 from __future__ import annotations
 
@@ -204,6 +206,41 @@ def run_timed(step, K: int, W: int, use_graph: bool):
     return ms_step, kern_ms, per
 
 
+def bench_torch_matmul(args):
+    """The vendor library's plain GEMM on the same shape, for comparison:
+    torch.matmul on BF16 (or FP16) operands, which runs hipBLASLt.  No FP8
+    decode, no block scales: a reference point for the matrix cores' rate,
+    not the block-scaled operation."""
+    import torch
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if args.dtype == "bf16" else torch.float16
+    M = N = K = 4096
+    gen = torch.Generator(device="cpu").manual_seed(2)
+    R = args.rotate or 8
+    ops = [(torch.randn(M, K, generator=gen).to(dt).to(dev),
+            torch.randn(K, N, generator=gen).to(dt).to(dev).t().contiguous().t(),   # stored N x K, as B
+            torch.empty(M, N, dtype=dt, device=dev)) for _ in range(R)]
+
+    def step(i, sh):                 # torch enqueues on its current stream, which is sh here
+        a, b, c = ops[i % R]
+        torch.matmul(a, b, out=c)
+
+    ms_step, kern_ms, _ = run_timed(step, args.steps, args.warmup, not args.no_graph)
+    flop = 2.0 * M * N * K
+    achieved = flop / (kern_ms * 1e-3) / 1e12
+    line = {"metric": f"vendor {args.dtype.upper()} GEMM TFLOPS (torch.matmul / hipBLASLt), same shape, for comparison",
+            "value": round(flop / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.dtype,
+            "data": "synthetic",
+            "config": {"workload": f"torch_matmul_4096_{args.dtype}", "M": M, "N": N, "K": K,
+                       "operand_copies": R, "launch": "eager" if args.no_graph else "hip_graph"},
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": None},
+            "cpu_baseline": None, "kernel_ms": round(kern_ms, 5)}
+    print(json.dumps(line), flush=True)
+
+
 def bench_quantize(args):
     import numpy as np
     import torch
@@ -262,7 +299,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the timed steps one by one from Python instead of replaying a HIP graph")
-    ap.add_argument("--op", choices=["gemm", "quantize"], default="gemm")
+    ap.add_argument("--op", choices=["gemm", "quantize", "torch-matmul"], default="gemm",
+                    help="torch-matmul: the vendor BF16/FP16 GEMM on 4096^3, for comparison")
+    ap.add_argument("--dtype", choices=["bf16", "fp16"], default="bf16", help="operand type of --op torch-matmul")
     ap.add_argument("--a-scale", choices=["128x128", "1x128"], default="128x128",
                     help="A scale blocks of the GEMM: 128x128, or one per token and 128 columns")
     ap.add_argument("--fmt", choices=["e4m3", "e5m2"], default="e4m3",
@@ -302,6 +341,9 @@ def main():
         return
     if args.op == "quantize":
         bench_quantize(args)
+        return
+    if args.op == "torch-matmul":
+        bench_torch_matmul(args)
         return
     dg.lib()
 
