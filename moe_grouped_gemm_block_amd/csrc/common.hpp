@@ -6,32 +6,12 @@
 
 namespace dg {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef float v16f __attribute__((ext_vector_type(16)));
 
 // Width of one K-block: the scale blocks are 128 x 128 (DeepGEMM FP8-for-MoE
-// page, section 2.1), and one 16x16x128 FP8 MFMA consumes exactly one K-block.
+// page, section 2.1), so every K-block's partial product is rescaled by one
+// A and one B factor.
 constexpr int KBLK = 128;
-
-// 16x16 output tile, K = 128 FP8 E4M3 products per element, FP32 result,
-// no input accumulator.  Zero E8M0 scale operands select the unscaled
-// v_mfma_f32_16x16x128_f8f6f4 encoding; format code 0 = FP8 E4M3 for both
-// operands.
-//
-// Register layout (identical for both operands): lane l supplies row / column
-// (l % 16) and the 32 consecutive K bytes [32 (l / 16), 32 (l / 16) + 32).
-// Output: lane l holds D[4 (l / 16) + r][l % 16], r = 0..3, where the first
-// index runs over `a`'s rows and the second over `b`'s rows.
-__device__ __forceinline__ v4f mfma16_fp8(const v8i& a, const v8i& b) {
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
-}
-
-// Same instruction, accumulating into `c`.
-__device__ __forceinline__ v4f mfma16_fp8_acc(const v8i& a, const v8i& b, const v4f& c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
 
 // FP32 -> BF16, round to nearest even (NaN stays NaN): gfx950 converts two
 // values per instruction (v_cvt_pk_bf16_f32).
@@ -88,14 +68,6 @@ __device__ __forceinline__ void store_row_span(void* C, size_t row_off, int n0, 
   }
 }
 
-// 16-byte granule swizzle inside a 128-byte LDS row: row r's granule g is
-// stored at slot g ^ ((r ^ (r >> 3)) & 7).  Eight consecutive rows, and the
-// two 8-row halves of sixteen consecutive rows, then hit distinct slots, so
-// the per-lane 16-byte reads of an MFMA fragment (16 rows, same granule) are
-// spread over all banks instead of piling onto one 16-byte column.  This is
-// the XOR row swizzle of the DeepGEMM FP8 kernel write-up (section 4.2),
-// re-derived for 16-byte granules.
-__device__ __forceinline__ int swz(int r, int g) { return g ^ ((r ^ (r >> 3)) & 7); }
 
 // Grouped GEMM: the expert owning row m0, i.e. the last e with
 // offs[e] <= m0 (empty experts are skipped automatically).  Returns G when
