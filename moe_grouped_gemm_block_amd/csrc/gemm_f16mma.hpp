@@ -38,7 +38,10 @@
 //   * per K-block and wave: FP8 fragments -> FP16 in registers, 4 chained
 //     16x16x32 FP16 MFMAs per 16 x 16 output tile give the block partial P,
 //     then acc = fma(sA*sB, P, acc) in FP32.  Wave sub-tiles never straddle
-//     a 128 x 128 scale block, so sA*sB is one scalar per wave and K-block;
+//     a 128 x 128 scale block, so sA*sB is one scalar per wave and K-block
+//     (with per-row A scales, one factor per row group: see ROW_SA);
+//   * the last K-block may be partial (K a multiple of 16): its copies past
+//     K read as zeros;
 //   * tiles are ordered so that each XCD (own L2) works on a compact group of
 //     row and column tiles.
 #pragma once
@@ -162,9 +165,9 @@ __device__ __forceinline__ void copy4_to_lds(const i32x4& rsrc, uint32_t voff, u
 
 struct GemmArgs {
   const uint8_t* A;       // [M][K]
-  const float* sA;        // [ceil(M/128)][K/128]
+  const float* sA;        // [ceil(M/128)][Kb], or [M][Kb] with per-row scales
   const uint8_t* B;       // [G][N][K]
-  const float* sB;        // [G][ceil(N/128)][K/128]
+  const float* sB;        // [G][ceil(N/128)][Kb]; Kb = ceil(K/128)
   void* C;                // [M][N]
   const int32_t* offs;    // [G+1] device, or nullptr for dense
   int G;

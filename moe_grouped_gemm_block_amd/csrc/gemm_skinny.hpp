@@ -26,9 +26,9 @@ namespace dg {
 // One few-rows problem: rows [0, M) of A / sA / C, one expert's B and sB.
 struct SkinnyJob {
   const uint8_t* A;       // [M][K]
-  const float* sA;        // [1][K/128] (one row block), or [M][K/128] with ROW_SA
+  const float* sA;        // [1][Kb] (one row block), or [M][Kb] with ROW_SA
   const uint8_t* B;       // [N][K]
-  const float* sB;        // [ceil(N/128)][K/128]
+  const float* sB;        // [ceil(N/128)][Kb]; Kb = ceil(K/128)
   void* C;                // [M][N]
   int M, N, K;
 };
@@ -44,7 +44,7 @@ constexpr int skinny_lds_bytes() {
 
 // The 16*NI columns from n0 of a few-rows problem, in the workgroup's LDS
 // buffer `lds` (skinny_lds_bytes bytes, 16-byte aligned).  ROW_SA: sA holds
-// one scale per row and K-block ([M][K/128]).
+// one scale per row and K-block ([M][Kb]).
 template <int MI, int NI, bool OUT_BF16, int FA = FMT_E4M3, int FB = FMT_E4M3, bool ROW_SA = false>
 __device__ __forceinline__ void gemm_skinny_body(const SkinnyJob& p, const int n0, uint8_t* lds) {
   constexpr int NW = 4;                         // waves, each a quarter of the K-blocks
