@@ -295,6 +295,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--shape", default="", metavar="M,N,K",
+                    help="a dense problem of this shape instead of a named workload (BF16 out, B ~ N(0, 0.02))")
     ap.add_argument("--rotate", type=int, default=0, help="operand copies (0 = enough to exceed the Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
@@ -348,7 +350,16 @@ def main():
     dg.lib()
 
     t0 = time.perf_counter()
-    p = I.make_config(args.workload, fmt=args.fmt, sa_rows=1 if args.a_scale == "1x128" else 128)
+    sa_rows = 1 if args.a_scale == "1x128" else 128
+    if args.shape:
+        M, N, K = (int(v) for v in args.shape.split(","))
+        p = I.dense_problem(M, N, K, seed=0, out_dtype="bf16", b_std=0.02, a_fmt=args.fmt, b_fmt=args.fmt,
+                            sa_rows=sa_rows, name=f"dense_{M}x{N}x{K}_{args.fmt}")
+    else:
+        p = I.make_config(args.workload, fmt=args.fmt, sa_rows=sa_rows)
+    # memory-bound: few rows (the few-rows kernel streams B once) or the decode step
+    hbm_bound = (p.M <= 64 and not p.grouped) if args.shape else args.workload in HBM_BOUND
+    gbs_value = hbm_bound if args.shape else args.workload in GBS_VALUE
     log(f"generated {p.name} in {time.perf_counter() - t0:.1f}s: M={p.M} N={p.N} K={p.K} "
         f"G={p.G} real_rows={p.real_rows}")
 
@@ -393,13 +404,13 @@ def main():
     ms_step, kern_ms, _ = run_timed(step, K, args.warmup, not args.no_graph)
 
     flop = p.algorithmic_flop()
-    if args.workload in GBS_VALUE:
+    if gbs_value:
         value = step_bytes / (ms_step * 1e-3) / 1e9
         unit = "GB/s"
     else:
         value = flop / (ms_step * 1e-3) / 1e12
         unit = "TFLOP/s"
-    if args.workload in HBM_BOUND:
+    if hbm_bound:
         achieved = step_bytes / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
