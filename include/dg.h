@@ -56,7 +56,8 @@
  *   - A failed kernel launch returns DG_ERR_LAUNCH.  Faults inside a kernel
  *     surface at the caller's next synchronisation, as for any HIP kernel.
  *   - Every call only enqueues kernels (no allocation, no memset, no host
- *     synchronisation), so it may be captured into a HIP graph and replayed.
+ *     synchronisation), so it may be captured into a HIP graph and replayed
+ *     (the DG_VALIDATE=1 debugging aid of the grouped calls excepted).
  *   - Results are bitwise repeatable: no atomics, and every output element
  *     is summed in a fixed order.
  *   - Out of scope: alpha / beta (C is overwritten, alpha = 1, beta = 0),
@@ -111,11 +112,18 @@ int dg_gemm_fp8_blockscaled(const void* A, const float* sA,
  *                   Empty experts (o_e == o_{e+1}) are allowed.
  *
  * Rows of a segment that the caller padded with zero codes come out as
- * exact zeros.  The offsets live on the device and are not validated (that
- * would need a device-to-host synchronisation): offsets that break the rules
- * above give undefined results.  Host-side errors: num_groups < 1 or
- * M_total not a multiple of 128 -> DG_ERR_INVALID_ARG; the shared rules
- * above otherwise.
+ * exact zeros.  The offsets live on the device and are not validated by
+ * default (that needs a device-to-host synchronisation): offsets that break
+ * the rules above give undefined values in C, but every access stays inside
+ * A, B, sA, sB and C (a tile's expert is found by a bounded binary search
+ * over the offsets).  Host-side errors: num_groups < 1 or M_total not a
+ * multiple of 128 -> DG_ERR_INVALID_ARG; the shared rules above otherwise.
+ *
+ * Debugging aid: with the environment variable DG_VALIDATE=1 (read once per
+ * process) the grouped calls first copy group_offsets to the host,
+ * synchronising `stream`, and return DG_ERR_INVALID_ARG for offsets that
+ * break the rules (DG_ERR_LAUNCH if that copy fails).  Such calls are no
+ * longer asynchronous and cannot be captured into a HIP graph.
  */
 int dg_grouped_gemm_fp8(const void* A, const float* sA,
                         const void* B, const float* sB,
@@ -190,8 +198,10 @@ int dg_grouped_gemm_fp8_ex(const void* A, int a_fmt, const float* sA, int sa_row
  * and an expert without rows costs nothing but reading its two offsets.
  * Longer segments are correct but re-stream B_e once per 64 rows (use
  * dg_grouped_gemm_fp8 for prefill-sized segments).  Offsets are not
- * validated on the host; the kernel clamps them into [0, M_total], so
- * offsets that break the rules give wrong rows but no out-of-bounds access.
+ * validated on the host (except under DG_VALIDATE=1, as for
+ * dg_grouped_gemm_fp8, here without the multiple-of-128 rule); the kernel
+ * clamps them into [0, M_total], so offsets that break the rules give wrong
+ * rows but no out-of-bounds access.
  * Host-side errors: num_groups < 1, unknown formats -> DG_ERR_INVALID_ARG;
  * the shared rules above otherwise (M_total need not be a multiple of 128).
  */

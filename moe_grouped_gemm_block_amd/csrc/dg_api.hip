@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <vector>
+
 #include "dg.h"
 // this translation unit defines the 1 x 8-wave variant and the quantiser; the
 // GEMM kernels of each operand-format pair are defined in kernels_*.hip
@@ -69,6 +71,34 @@ int tail_tile() {
     return e ? atoi(e) : 256;
   }();
   return v;
+}
+
+// DG_VALIDATE=1 (read once per process): grouped calls first copy
+// group_offsets to the host, synchronising `stream`, and reject offsets that
+// break the layout rules with DG_ERR_INVALID_ARG.  A debugging aid: the call
+// is then no longer asynchronous and cannot be captured into a graph.
+bool validate_offsets() {
+  static const bool v = [] {
+    const char* e = getenv("DG_VALIDATE");
+    return e != nullptr && atoi(e) != 0;
+  }();
+  return v;
+}
+
+// 0 = o_0 <= o_1 <= ... <= o_G = M_total, and every o_e a multiple of 128
+// when the segments are padded.
+int check_offsets(const int32_t* offs, int G, int64_t M_total, bool padded, hipStream_t stream) {
+  if (!validate_offsets()) return DG_OK;
+  std::vector<int32_t> h(size_t(G) + 1);
+  if (hipMemcpyAsync(h.data(), offs, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return DG_ERR_LAUNCH;
+  if (h[0] != 0 || int64_t(h[size_t(G)]) != M_total) return DG_ERR_INVALID_ARG;
+  for (int g = 0; g < G; ++g) {
+    if (h[size_t(g) + 1] < h[size_t(g)]) return DG_ERR_INVALID_ARG;
+    if (padded && h[size_t(g) + 1] % dg::KBLK != 0) return DG_ERR_INVALID_ARG;
+  }
+  return DG_OK;
 }
 
 // One launch over the 128-row tiles [m_tile0, m_tile0 + m_tiles).
@@ -226,6 +256,8 @@ int grouped_impl(const void* A, int a_fmt, const float* sA, int sa_rows, const v
   int st = check_common(A, sA, B, sB, C, M_total, N, K, out_dtype);
   if (st != DG_OK || M_total == 0 || N == 0) return st;
   if (group_offsets == nullptr || !aligned(group_offsets, 4)) return DG_ERR_INVALID_ARG;
+  st = check_offsets(group_offsets, num_groups, M_total, true, stream);
+  if (st != DG_OK) return st;
   dg::GemmArgs a{};
   a.A = static_cast<const uint8_t*>(A);
   a.sA = sA;
@@ -252,6 +284,8 @@ int dg_grouped_gemm_fp8_segments(const void* A, int a_fmt, const float* sA, cons
   int st = check_common(A, sA, B, sB, C, M_total, N, K, out_dtype);
   if (st != DG_OK || M_total == 0 || N == 0) return st;
   if (group_offsets == nullptr || !aligned(group_offsets, 4)) return DG_ERR_INVALID_ARG;
+  st = check_offsets(group_offsets, num_groups, M_total, false, stream);
+  if (st != DG_OK) return st;
   dg::GemmArgs a{};
   a.A = static_cast<const uint8_t*>(A);
   a.sA = sA;

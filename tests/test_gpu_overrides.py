@@ -27,3 +27,16 @@ def test_tile_override(env):
                        capture_output=True, text=True, timeout=240)
     print(r.stdout, file=sys.stderr)
     assert r.returncode == 0, r.stdout + r.stderr[-2000:]
+
+
+def test_validate_offsets():
+    """DG_VALIDATE=1: valid offsets give correct results, invalid ones are
+    rejected on the host before any launch (tests/validate_child.py)."""
+    full = dict(os.environ)
+    full.pop("DG_FORCE_TILE", None)
+    full.pop("DG_TAIL_TILE", None)
+    full["DG_VALIDATE"] = "1"
+    r = subprocess.run([sys.executable, os.path.join(HERE, "validate_child.py")], env=full,
+                       capture_output=True, text=True, timeout=240)
+    print(r.stdout, file=sys.stderr)
+    assert r.returncode == 0, r.stdout + r.stderr[-2000:]
