@@ -93,6 +93,18 @@ __device__ __forceinline__ void fp8x32_to_f16(const int4& r0, const int4& r1, v8
   }
 }
 
+// MFMA operand st (bytes 8st .. 8st+7 of a lane's 32) of the raw fragment
+// pair r0 (bytes 0..15), r1 (bytes 16..31), as eight FP16 values.
+template <int FMT = FMT_E4M3>
+__device__ __forceinline__ v8h fp8_operand(const int4& r0, const int4& r1, int st) {
+  const int4& r = st < 2 ? r0 : r1;
+  const uint32_t w0 = uint32_t((st & 1) ? r.z : r.x), w1 = uint32_t((st & 1) ? r.w : r.y);
+  uint32_t h[4];
+  fp8x4_to_f16<FMT>(w0, h[0], h[1]);
+  fp8x4_to_f16<FMT>(w1, h[2], h[3]);
+  return __builtin_bit_cast(v8h, (uint4{h[0], h[1], h[2], h[3]}));
+}
+
 __device__ __forceinline__ v4f mfma16_f16(const v8h& a, const v8h& b, const v4f& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -346,35 +358,67 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
     const uint8_t* la = lds + stage * A_BYTES;
     const uint8_t* lb = lds + 2 * A_BYTES + stage * B_BYTES;
 
-    // A fragments (MFMA second operand): rows wm + 16 mi + r16, bytes [32q, 32q+32)
-    v8h af[MI][4];
+    // Raw FP8 fragments, all read before the first wait: A rows
+    // wm + 16 mi + r16 (the MFMA's second operand), bytes [32q, 32q+32), and
+    // the first two B column tiles.
+    int4 xa0[MI], xa1[MI];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-      const int4 x0 = *reinterpret_cast<const int4*>(la + a_off0 + mi * 16 * KBLK);
-      const int4 x1 = *reinterpret_cast<const int4*>(la + a_off1 + mi * 16 * KBLK);
-      fp8x32_to_f16<FA>(x0, x1, af[mi]);
+      xa0[mi] = *reinterpret_cast<const int4*>(la + a_off0 + mi * 16 * KBLK);
+      xa1[mi] = *reinterpret_cast<const int4*>(la + a_off1 + mi * 16 * KBLK);
     }
-    // B column tiles, software-pipelined: while the MFMAs of tile ni consume
-    // operand st, operand st of tile ni+1 is converted into the registers
-    // they free, and the FP32 rescale of tile ni-1 is threaded between the
-    // first MFMAs of tile ni.  Raw FP8 of tile ni+2 is read from LDS one tile
-    // ahead.
     int4 y0 = *reinterpret_cast<const int4*>(lb + b_off0);
     int4 y1 = *reinterpret_cast<const int4*>(lb + b_off1);
-    v8h bf[4];
-    fp8x32_to_f16<FB>(y0, y1, bf);
+    int4 z0 = y0, z1 = y1;
     if (NI > 1) {
-      y0 = *reinterpret_cast<const int4*>(lb + b_off0 + 16 * KBLK);
-      y1 = *reinterpret_cast<const int4*>(lb + b_off1 + 16 * KBLK);
+      z0 = *reinterpret_cast<const int4*>(lb + b_off0 + 16 * KBLK);
+      z1 = *reinterpret_cast<const int4*>(lb + b_off1 + 16 * KBLK);
     }
+    v8h af[MI][4];
+    v8h bf[4];
     v4f part[MI];
+    // Column tile 0, k-step by k-step: each A operand is converted just
+    // before its first MFMA, so the matrix core starts after a few
+    // conversions instead of after all of A.  The B operands of tile 1 are
+    // converted into the registers each k-step frees, and the raw bytes of
+    // tile 2 are read into those of tile 0.
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
+    for (int st = 0; st < 4; ++st) {
+      bf[st] = fp8_operand<FB>(y0, y1, st);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        af[mi][st] = fp8_operand<FA>(xa0[mi], xa1[mi], st);
+        part[mi] = mfma16_f16(bf[st], af[mi][st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : part[mi]);
+      }
+      if (NI > 1) {
+        bf[st] = fp8_operand<FB>(z0, z1, st);
+        if (NI > 2 && st == 1) y0 = *reinterpret_cast<const int4*>(lb + b_off0 + 2 * 16 * KBLK);
+        if (NI > 2 && st == 3) y1 = *reinterpret_cast<const int4*>(lb + b_off1 + 2 * 16 * KBLK);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * MI + (NI > 1 ? 4 : 2), 0);   // raw reads first
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                       // B operand of tile 0
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                     // A operand
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // 1 MFMA
+      }
+      if (NI > 1) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);           // B operand of tile 1
+    }
+    // Column tiles 1 .. NI-1, software-pipelined: while the MFMAs of tile ni
+    // consume operand st, operand st of tile ni+1 is converted into the
+    // registers they free, and the FP32 rescale of tile ni-1 is threaded
+    // between the first MFMAs of tile ni.  Raw FP8 of tile ni+2 is read from
+    // LDS one tile ahead.
+#pragma unroll
+    for (int ni = 1; ni < NI; ++ni) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
-          if (st == 0 && ni > 0) {
+          if (st == 0) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               acc[mi][ni - 1][r] = __builtin_fmaf(s_m[mi], part[mi][r], acc[mi][ni - 1][r]);
@@ -382,13 +426,7 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
           part[mi] = mfma16_f16(bf[st], af[mi][st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : part[mi]);
         }
         if (ni + 1 < NI) {
-          // operand st of tile ni+1: raw dwords 2st, 2st+1
-          const int4& y = st < 2 ? y0 : y1;
-          const uint32_t w0 = uint32_t((st & 1) ? y.z : y.x), w1 = uint32_t((st & 1) ? y.w : y.y);
-          uint32_t h[4];
-          fp8x4_to_f16<FB>(w0, h[0], h[1]);
-          fp8x4_to_f16<FB>(w1, h[2], h[3]);
-          bf[st] = __builtin_bit_cast(v8h, (uint4{h[0], h[1], h[2], h[3]}));
+          bf[st] = fp8_operand<FB>(y0, y1, st);   // operand st of tile ni+1
           if (ni + 2 < NI && st == 1)
             y0 = *reinterpret_cast<const int4*>(lb + b_off0 + (ni + 2) * 16 * KBLK);
           if (ni + 2 < NI && st == 3)
@@ -396,14 +434,10 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
         }
       }
       // pin the interleave: rescale / MFMA alternation, then MFMA / convert
-      if (ni > 0) {
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU (rescale)
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-        }
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      for (int mi = 0; mi < MI; ++mi) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU (rescale)
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
       }
       if (ni + 1 < NI) {
 #pragma unroll
