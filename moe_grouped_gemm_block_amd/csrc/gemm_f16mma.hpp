@@ -33,8 +33,12 @@
 //     spread over the banks and every read of a wave is one base register
 //     plus an immediate offset;
 //   * B rows are permuted on their way into LDS so that, with B as the MFMA's
-//     first operand, each lane ends up holding 32 consecutive columns of one
-//     output row: the epilogue writes whole 16-byte vectors;
+//     first operand, each lane ends up holding four runs of 8 consecutive
+//     columns of one output row, 32 columns apart, and the four lanes of a
+//     row hold adjacent runs: every 16-byte store instruction of the
+//     epilogue writes whole 64-byte pieces of C rows (16-byte pieces with
+//     gaps come back through partial writes of the HBM and cost about twice
+//     the time);
 //   * per K-block and wave: FP8 fragments -> FP16 in registers, 4 chained
 //     16x16x32 FP16 MFMAs per 16 x 16 output tile give the block partial P,
 //     then acc = fma(sA*sB, P, acc) in FP32.  Wave sub-tiles never straddle
@@ -268,8 +272,9 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   const uint32_t a_lane = uint32_t(lr * K + gsl);
   // B: LDS row r = 8c + L/8 holds, inside column half h = r / 128, operand
   // row ii = r % 16 of MFMA column tile ni = (r % 128) / 16, i.e. the tile
-  // row 128 h + 32 (ii / 4) + 4 ni + ii % 4.
-  const uint32_t b_lane = uint32_t((32 * (lane >> 5) + (lr & 3)) * K + gsl);
+  // row 128 h + 32 (ni / 2) + 8 (ii / 4) + 4 (ni % 2) + ii % 4.  With
+  // ii = 8 (c % 2) + L/8, the lane contributes 8 (L / 32) + (L/8) % 4.
+  const uint32_t b_lane = uint32_t((8 * (lane >> 5) + (lr & 3)) * K + gsl);
 
   // LDS byte address of the buffer (wave-uniform)
   const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
@@ -289,7 +294,7 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       const int c = wave + NW * i;
-      const int row = 128 * (c >> 4) + 64 * (c & 1) + 4 * ((c & 15) >> 1);
+      const int row = 128 * (c >> 4) + 32 * ((c & 15) >> 2) + 16 * (c & 1) + 4 * ((c >> 1) & 1);
       const uint32_t voff = b_kb + uint32_t(row * K);
       copy16_to_lds(rB, voff, lds_addr + uint32_t(2 * A_BYTES + stage * B_BYTES + c * 1024));
     }
@@ -462,21 +467,24 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds C[m][n0 + wn + 32 q + 0 .. 31] ------------------
-  constexpr int CW = WN / 4;                   // consecutive columns per lane
+  // ---- epilogue: column tiles 2j and 2j+1 of a lane hold
+  // C[m][n0 + wn + 32 j + 8 q + 0 .. 7] ------------------------------------
   const int lane_e = lane_id();
   const int q_e = lane_e >> 4, r16_e = lane_e & 15;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
     const int m = m0 + wm + mi * 16 + r16_e;
     if (m >= M) continue;
-    const int nbase = n0 + wn + q_e * CW;
-    float v[CW];
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
+    for (int j = 0; j < NI / 2; ++j) {
+      float v[8];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[ni * 4 + r] = acc[mi][ni][r];
-    store_row_span<OUT_BF16, CW>(p.C, size_t(m) * N, nbase, N, v);
+      for (int r = 0; r < 4; ++r) {
+        v[r] = acc[mi][2 * j][r];
+        v[4 + r] = acc[mi][2 * j + 1][r];
+      }
+      store_row_span<OUT_BF16, 8>(p.C, size_t(m) * N, n0 + wn + 32 * j + 8 * q_e, N, v);
+    }
   }
 }
 
