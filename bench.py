@@ -14,8 +14,12 @@ One JSON line is printed on stdout.  `value` is throughput over the timed
 region (TFLOP/s of algorithmic work = 2 * real_rows * N * K, or GB/s of
 algorithmic bytes for the memory-bound skinny shape).  `roofline.achieved`
 uses the kernel's average duration from HIP events recorded on the launch
-stream around every timed step.  `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workload on this host.
+stream around the timed steps.  `kernel_ms_eager` is the same kernel timed
+with launches one by one after the timed region: rocprofv3's kernel trace
+reports that duration per dispatch (graph-launched ones included), so it is
+the figure that the committed profile summaries agree with.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload
+on this host.
 
 Workloads (seeded, synthetic; see inputs.make_config):
   1  dense 256^3, FP32 out                      (parity case)
@@ -206,6 +210,18 @@ def run_timed(step, K: int, W: int, use_graph: bool):
     return ms_step, kern_ms, per
 
 
+def eager_kernel_ms(step, K: int, use_graph: bool):
+    """Per-launch kernel time with the steps launched one by one (HIP events
+    on the launch stream), measured after the timed region.  This is the
+    duration rocprofv3's kernel trace reports per dispatch, also for
+    graph-launched kernels, so it is the figure to compare with the committed
+    profile summaries.  None when the timed region itself was eager."""
+    if not use_graph:
+        return None
+    _, ms, _ = run_timed(step, min(K, 50), 5, False)
+    return round(ms, 5)
+
+
 def bench_torch_matmul(args):
     """The vendor library's plain GEMM on the same shape, for comparison:
     torch.matmul on BF16 (or FP16) operands, which runs hipBLASLt.  No FP8
@@ -274,6 +290,7 @@ def bench_quantize(args):
 
     n = args.steps
     ms_step, kern_ms, _ = run_timed(step, n, args.warmup, not args.no_graph)
+    kern_eager = eager_kernel_ms(step, n, not args.no_graph)
     name = f"quantize_{M}x{K}_bf16_{R_blk}x128"
     achieved = step_bytes / (kern_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -285,7 +302,8 @@ def bench_quantize(args):
             "data": "synthetic",
             "config": {"workload": name, "M": M, "K": K, "block_rows": R_blk, "seed": 2, "operand_copies": R,
                        "launch": "eager" if args.no_graph else "hip_graph"},
-            "roofline": roof, "cpu_baseline": cpu, "kernel_ms": round(kern_ms, 5)}
+            "roofline": roof, "cpu_baseline": cpu, "kernel_ms": round(kern_ms, 5),
+            "kernel_ms_eager": kern_eager}
     print(json.dumps(line), flush=True)
 
 
@@ -402,6 +420,7 @@ def main():
 
     K = args.steps
     ms_step, kern_ms, _ = run_timed(step, K, args.warmup, not args.no_graph)
+    kern_eager = eager_kernel_ms(step, K, not args.no_graph)
 
     flop = p.algorithmic_flop()
     if gbs_value:
@@ -450,7 +469,7 @@ def main():
             "dtype": "fp8_e4m3" if p.a_fmt == p.b_fmt == "e4m3" else f"fp8_{p.a_fmt}x{p.b_fmt}",
             "data": "synthetic",
             "config": cfg, "roofline": roof, "cpu_baseline": cpu,
-            "kernel_ms": round(kern_ms, 5)}
+            "kernel_ms": round(kern_ms, 5), "kernel_ms_eager": kern_eager}
     print(json.dumps(line), flush=True)
 
 
