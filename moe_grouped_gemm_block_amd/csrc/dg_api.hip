@@ -50,9 +50,13 @@ int check_common(const void* A, const float* sA, const void* B, const float* sB,
 // 128 x 512 tile runs 8 waves (two per SIMD, one workgroup per CU, 160 KB of
 // LDS); the 128 x 256 tile runs 4 waves, serves narrow problems and finishes
 // the last partial round of a large problem (see launch()); the 128 x 128
-// tile (2 waves, 64 KB of LDS) is the alternative for that last round.
+// tile (2 waves, 64 KB of LDS) is the alternative for that last round.  The
+// 256 x 256 tile (8 waves, 128 KB of LDS) computes bit-identical results to
+// 128 x 512 and copies 20 % fewer bytes per K-block; it takes dense problems
+// whose 256 x 256 tiles fill whole rounds of the CUs (4096^3, 8192^2 x K, ...).
 // DG_FORCE_TILE=512, 256 or 128 uses that tile for every problem (few rows
-// included), 1512 selects the 1 x 8 wave arrangement where it applies;
+// included), 2256 the 256 x 256 tile for every dense problem, 1512 selects
+// the 1 x 8 wave arrangement where it applies;
 // DG_TAIL_TILE=0 / 128 / 256 switches off or sets the tile of the last
 // partial round (tuning aids).
 constexpr int kCUs = 256;
@@ -101,7 +105,8 @@ int check_offsets(const int32_t* offs, int G, int64_t M_total, bool padded, hipS
   return DG_OK;
 }
 
-// One launch over the 128-row tiles [m_tile0, m_tile0 + m_tiles).
+// One launch over the row tiles [m_tile0, m_tile0 + m_tiles) of the kernel's
+// tile height (128 rows unless stated; m_tiles < 0: all 128-row tiles).
 int launch_tiles(dg::GemmArgs a, int bn, int threads, void (*k_bf16)(dg::GemmArgs),
                  void (*k_f32)(dg::GemmArgs), int out_dtype, hipStream_t stream, int m_tile0 = 0,
                  int m_tiles = -1) {
@@ -122,11 +127,12 @@ typedef void (*kfn)(dg::GemmArgs);
 
 // Kernels of one pair of operand formats; combo = 2 * a_fmt + b_fmt.  The
 // *rs kernels take one A scale per row (1 x 128 blocks).
-struct TiledSet { kfn k512[2], k256[2], k128[2]; };   // [f32, bf16]
+struct TiledSet { kfn k512[2], k256[2], k128[2], k256sq[2]; };   // [f32, bf16]
 #define DG_TILED_SET(SFX)                                                   \
   {{dg::dg_gemm_128x512_f32##SFX, dg::dg_gemm_128x512_bf16##SFX},           \
    {dg::dg_gemm_128x256_f32##SFX, dg::dg_gemm_128x256_bf16##SFX},           \
-   {dg::dg_gemm_128x128_f32##SFX, dg::dg_gemm_128x128_bf16##SFX}}
+   {dg::dg_gemm_128x128_f32##SFX, dg::dg_gemm_128x128_bf16##SFX},           \
+   {dg::dg_gemm_256x256_f32##SFX, dg::dg_gemm_256x256_bf16##SFX}}
 // [A scales per 128 x 128 block / per row][combo]
 const TiledSet kTiled[2][4] = {
     {DG_TILED_SET(), DG_TILED_SET(_a4b5), DG_TILED_SET(_a5b4), DG_TILED_SET(_a5b5)},
@@ -201,6 +207,11 @@ int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, int row_s
     return launch_tiles(a, 512, 512, dg::dg_gemm_wide_128x512_bf16, dg::dg_gemm_wide_128x512_f32, out_dtype,
                         stream);
   if (forced_tile() == 128) return launch_tiles(a, 128, 128, ks.k128[1], ks.k128[0], out_dtype, stream);
+  if (a.offs == nullptr) {
+    const int64_t m256 = (int64_t(a.M) + 255) / 256, t256 = m256 * ((int64_t(a.N) + 255) / 256);
+    if (forced_tile() == 2256 || (forced_tile() == 0 && a.M % 256 == 0 && t256 % kCUs == 0))
+      return launch_tiles(a, 256, 512, ks.k256sq[1], ks.k256sq[0], out_dtype, stream, 0, int(m256));
+  }
   if (use512 && forced_tile() == 0 && tail_tile() != 0) {
     // A 128 x 512 tile takes about as long whether 1 or all 256 CUs are busy,
     // so a last round that is only partly filled costs almost a full round.

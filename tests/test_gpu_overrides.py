@@ -1,5 +1,6 @@
 """The tile-choice overrides (DG_FORCE_TILE: 1512 = the 1 x 8-wave variant,
-512 / 256 / 128 = one tile shape for every problem; DG_TAIL_TILE: 0 = no
+512 / 256 / 128 = one tile shape for every problem, 2256 = the 256 x 256
+tile for every dense problem; DG_TAIL_TILE: 0 = no
 separate last round, 128 = 128 x 128 tiles for it) give results inside the
 parity bound.  The library reads them once per process, so every setting
 runs tests/override_child.py in a child process.  Needs a GPU."""
@@ -15,6 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 @pytest.mark.parametrize("env", [{"DG_FORCE_TILE": "1512"}, {"DG_FORCE_TILE": "512"},
+                                 {"DG_FORCE_TILE": "2256"},
                                  {"DG_FORCE_TILE": "256"}, {"DG_FORCE_TILE": "128"},
                                  {"DG_TAIL_TILE": "0"}, {"DG_TAIL_TILE": "128"}],
                          ids=lambda e: "_".join(f"{k}={v}" for k, v in e.items()))

@@ -236,6 +236,19 @@ def test_grouped_configs_sampled(i):
         assert np.all(Cg[lo:off[e + 1]] == 0)
 
 
+# ----------------------------------------------------------------- 256 x 256 tiles
+# Dense problems whose 256 x 256 tiles fill whole rounds of the 256 CUs run on
+# that tile (4096 x 4096: 16 x 16 tiles); compared in full at small K, one
+# case with a partial last K-block.
+
+@pytest.mark.parametrize("K,out", [(128, "f32"), (272, "bf16")])
+def test_square_tile_dense_full(K, out):
+    M = N = 4096
+    log(f"256x256 tile dense {M}x{N}x{K} {out}")
+    p = I.dense_problem(M, N, K, seed=K, out_dtype=out, block_log2_range=3.0)
+    check(p, as64(run(p)), what=f"256x256 K={K} {out}")
+
+
 # ----------------------------------------------------------------- last-round split
 # 33 row tiles x 8 column tiles of 128 x 512 = 264 tiles: the first 32 row tiles
 # fill one round of 256 CUs, the 33rd runs as narrower tiles in a second
