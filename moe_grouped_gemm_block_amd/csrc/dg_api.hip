@@ -46,19 +46,22 @@ int check_common(const void* A, const float* sA, const void* B, const float* sB,
   return DG_OK;
 }
 
-// Tile shape of one launch.  Every wave owns a 64 x 128 sub-tile.  The
-// 128 x 512 tile runs 8 waves (two per SIMD, one workgroup per CU, 160 KB of
-// LDS); the 128 x 256 tile runs 4 waves, serves narrow problems and finishes
-// the last partial round of a large problem (see launch()); the 128 x 128
+// Tile shape of one launch.  Every wave owns a 64 x 128 sub-tile, except in
+// the 8-wave 128 x 256 tile (64 x 64).  The 128 x 512 tile runs 8 waves (two
+// per SIMD, one workgroup per CU, 160 KB of LDS); the 128 x 256 tile runs 4
+// or 8 waves (see launch_256), serves narrow problems and finishes the last
+// partial round of a large problem (see launch()); the 128 x 128
 // tile (2 waves, 64 KB of LDS) is the alternative for that last round.  The
 // 256 x 256 tile (8 waves, 128 KB of LDS) computes bit-identical results to
 // 128 x 512 and copies 20 % fewer bytes per K-block; it takes dense problems
 // whose 256 x 256 tiles fill whole rounds of the CUs (4096^3, 8192^2 x K, ...).
 // DG_FORCE_TILE=512, 256 or 128 uses that tile for every problem (few rows
 // included), 2256 the 256 x 256 tile for every dense problem, 1512 selects
-// the 1 x 8 wave arrangement where it applies;
-// DG_TAIL_TILE=0 / 128 / 256 switches off or sets the tile of the last
-// partial round (tuning aids).
+// the 1 x 8 wave arrangement where it applies, 8256 the 8-wave 128 x 256
+// tile wherever a 128 x 256 tile is used (256: the 4-wave one);
+// DG_TAIL_TILE=0 / 128 / 256 / 8256 switches off or sets the tile of the
+// last partial round (256: 128 x 256, 4 or 8 waves as launch_256 picks;
+// 8256: always 8 waves) (tuning aids).
 constexpr int kCUs = 256;
 
 int forced_tile() {
@@ -127,12 +130,13 @@ typedef void (*kfn)(dg::GemmArgs);
 
 // Kernels of one pair of operand formats; combo = 2 * a_fmt + b_fmt.  The
 // *rs kernels take one A scale per row (1 x 128 blocks).
-struct TiledSet { kfn k512[2], k256[2], k128[2], k256sq[2]; };   // [f32, bf16]
+struct TiledSet { kfn k512[2], k256[2], k128[2], k256sq[2], k256w8[2]; };   // [f32, bf16]
 #define DG_TILED_SET(SFX)                                                   \
   {{dg::dg_gemm_128x512_f32##SFX, dg::dg_gemm_128x512_bf16##SFX},           \
    {dg::dg_gemm_128x256_f32##SFX, dg::dg_gemm_128x256_bf16##SFX},           \
    {dg::dg_gemm_128x128_f32##SFX, dg::dg_gemm_128x128_bf16##SFX},           \
-   {dg::dg_gemm_256x256_f32##SFX, dg::dg_gemm_256x256_bf16##SFX}}
+   {dg::dg_gemm_256x256_f32##SFX, dg::dg_gemm_256x256_bf16##SFX},           \
+   {dg::dg_gemm_128x256w8_f32##SFX, dg::dg_gemm_128x256w8_bf16##SFX}}
 // [A scales per 128 x 128 block / per row][combo]
 const TiledSet kTiled[2][4] = {
     {DG_TILED_SET(), DG_TILED_SET(_a4b5), DG_TILED_SET(_a5b4), DG_TILED_SET(_a5b5)},
@@ -192,6 +196,21 @@ int launch_segments(dg::GemmArgs a, int out_dtype, int combo, hipStream_t stream
   return err == hipSuccess ? DG_OK : DG_ERR_LAUNCH;
 }
 
+// 128 x 256 tiles over the row tiles [m_tile0, m_tile0 + m_tiles) (all when
+// m_tiles < 0).  With at most half as many workgroups as CUs every tile runs
+// alone on its CU and its latency is the launch's time: the 8-wave tile
+// (64 x 64 per wave, two waves per SIMD) finishes it sooner.  With more
+// workgroups the chip runs at its power limit and the 4-wave tile's fewer
+// conversions per MFMA (1.5 instead of 2) win.
+int launch_256(const dg::GemmArgs& a, const TiledSet& ks, int out_dtype, hipStream_t stream, int m_tile0 = 0,
+               int m_tiles = -1) {
+  const int64_t rows = m_tiles >= 0 ? m_tiles : (int64_t(a.M) + 127) / 128;
+  const int64_t blocks = rows * ((int64_t(a.N) + 255) / 256);
+  if (forced_tile() == 8256 || tail_tile() == 8256 || (forced_tile() != 256 && blocks <= kCUs / 2))
+    return launch_tiles(a, 256, 512, ks.k256w8[1], ks.k256w8[0], out_dtype, stream, m_tile0, m_tiles);
+  return launch_tiles(a, 256, 256, ks.k256[1], ks.k256[0], out_dtype, stream, m_tile0, m_tiles);
+}
+
 int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, int row_sa, hipStream_t stream) {
   const int combo = 2 * a_fmt + b_fmt;
   const TiledSet& ks = kTiled[row_sa][combo];
@@ -207,6 +226,7 @@ int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, int row_s
     return launch_tiles(a, 512, 512, dg::dg_gemm_wide_128x512_bf16, dg::dg_gemm_wide_128x512_f32, out_dtype,
                         stream);
   if (forced_tile() == 128) return launch_tiles(a, 128, 128, ks.k128[1], ks.k128[0], out_dtype, stream);
+  if (forced_tile() == 8256) return launch_256(a, ks, out_dtype, stream);
   if (a.offs == nullptr) {
     const int64_t m256 = (int64_t(a.M) + 255) / 256, t256 = m256 * ((int64_t(a.N) + 255) / 256);
     if (forced_tile() == 2256 || (forced_tile() == 0 && a.M % 256 == 0 && t256 % kCUs == 0))
@@ -228,11 +248,11 @@ int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, int row_s
       const int rest = int(m_tiles - main_m);
       if (tail_tile() == 128)
         return launch_tiles(a, 128, 128, ks.k128[1], ks.k128[0], out_dtype, stream, int(main_m), rest);
-      return launch_tiles(a, 256, 256, ks.k256[1], ks.k256[0], out_dtype, stream, int(main_m), rest);
+      return launch_256(a, ks, out_dtype, stream, int(main_m), rest);
     }
   }
   if (use512) return launch_tiles(a, 512, 512, ks.k512[1], ks.k512[0], out_dtype, stream);
-  return launch_tiles(a, 256, 256, ks.k256[1], ks.k256[0], out_dtype, stream);
+  return launch_256(a, ks, out_dtype, stream);
 }
 
 bool valid_fmt(int f) { return f == DG_FP8_E4M3 || f == DG_FP8_E5M2; }

@@ -219,9 +219,11 @@ __device__ __forceinline__ void tile_of(int bid, int m_tiles, int n_tiles, int& 
 // loads the scales of its four rows one K-block ahead with ordinary vector
 // loads: the loop drains every copy (vmcnt(0)) at the end of each K-block
 // anyway, so waiting for these loads costs nothing, and no LDS is needed.
-template <int NWM, int NWN, bool OUT_BF16, int FA = FMT_E4M3, int FB = FMT_E4M3, bool ROW_SA = false>
+template <int NWM, int NWN, bool OUT_BF16, int FA = FMT_E4M3, int FB = FMT_E4M3, bool ROW_SA = false,
+          int WN = 128>
 __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
-  constexpr int WM = 64, WN = 128;             // wave sub-tile
+  static_assert(WN == 128 || WN == 64, "wave sub-tile width");
+  constexpr int WM = 64;                       // wave sub-tile: WM x WN
   constexpr int MI = WM / 16, NI = WN / 16;    // 16x16 MFMA tiles per wave
   constexpr int NW = NWM * NWN;                // waves per workgroup
   constexpr int BM = NWM * WM, BN = NWN * WN;  // workgroup tile
@@ -496,24 +498,26 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
 // One named kernel per tile shape, output type and pair of operand formats
 // (suffix _a<A format>b<B format>, 4 = E4M3, 5 = E5M2; E4M3 x E4M3 keeps the
 // plain name); suffix _rs: row-scaled A (1 x 128 scales).
-#define DG_GEMM_KERNEL_DEF(NAME, NWM, NWN, BF16, FA, FB, RS)                \
+#define DG_GEMM_KERNEL_DEF(NAME, NWM, NWN, WN, BF16, FA, FB, RS)            \
   __global__ __launch_bounds__(64 * NWM * NWN, 1) void NAME(GemmArgs p) {   \
-    gemm_f16mma_body<NWM, NWN, BF16, FA, FB, RS>(p);                        \
+    gemm_f16mma_body<NWM, NWN, BF16, FA, FB, RS, WN>(p);                    \
   }
-#define DG_GEMM_KERNEL_DECL(NAME, NWM, NWN, BF16, FA, FB, RS) \
+#define DG_GEMM_KERNEL_DECL(NAME, NWM, NWN, WN, BF16, FA, FB, RS) \
   __global__ __launch_bounds__(64 * NWM * NWN, 1) void NAME(GemmArgs p);
-#define DG_GEMM_SHAPE(K, SHAPE, NWM, NWN, SFX, FA, FB, RS)                  \
-  K(dg_gemm_##SHAPE##_bf16##SFX, NWM, NWN, true, FA, FB, RS)                \
-  K(dg_gemm_##SHAPE##_f32##SFX, NWM, NWN, false, FA, FB, RS)
+#define DG_GEMM_SHAPE(K, SHAPE, NWM, NWN, WN, SFX, FA, FB, RS)              \
+  K(dg_gemm_##SHAPE##_bf16##SFX, NWM, NWN, WN, true, FA, FB, RS)            \
+  K(dg_gemm_##SHAPE##_f32##SFX, NWM, NWN, WN, false, FA, FB, RS)
 #define DG_GEMM_FORMATS(K, SFX, FA, FB)                                     \
-  DG_GEMM_SHAPE(K, 128x512, 2, 4, SFX, FA, FB, false)                       \
-  DG_GEMM_SHAPE(K, 256x256, 4, 2, SFX, FA, FB, false)                       \
-  DG_GEMM_SHAPE(K, 128x256, 2, 2, SFX, FA, FB, false)                       \
-  DG_GEMM_SHAPE(K, 128x128, 2, 1, SFX, FA, FB, false)                       \
-  DG_GEMM_SHAPE(K, 128x512, 2, 4, SFX##_rs, FA, FB, true)                   \
-  DG_GEMM_SHAPE(K, 256x256, 4, 2, SFX##_rs, FA, FB, true)                   \
-  DG_GEMM_SHAPE(K, 128x256, 2, 2, SFX##_rs, FA, FB, true)                   \
-  DG_GEMM_SHAPE(K, 128x128, 2, 1, SFX##_rs, FA, FB, true)
+  DG_GEMM_SHAPE(K, 128x512, 2, 4, 128, SFX, FA, FB, false)                  \
+  DG_GEMM_SHAPE(K, 256x256, 4, 2, 128, SFX, FA, FB, false)                  \
+  DG_GEMM_SHAPE(K, 128x256, 2, 2, 128, SFX, FA, FB, false)                  \
+  DG_GEMM_SHAPE(K, 128x256w8, 2, 4, 64, SFX, FA, FB, false)                 \
+  DG_GEMM_SHAPE(K, 128x128, 2, 1, 128, SFX, FA, FB, false)                  \
+  DG_GEMM_SHAPE(K, 128x512, 2, 4, 128, SFX##_rs, FA, FB, true)              \
+  DG_GEMM_SHAPE(K, 256x256, 4, 2, 128, SFX##_rs, FA, FB, true)              \
+  DG_GEMM_SHAPE(K, 128x256, 2, 2, 128, SFX##_rs, FA, FB, true)              \
+  DG_GEMM_SHAPE(K, 128x256w8, 2, 4, 64, SFX##_rs, FA, FB, true)             \
+  DG_GEMM_SHAPE(K, 128x128, 2, 1, 128, SFX##_rs, FA, FB, true)
 DG_GEMM_FORMATS(DG_KERNEL(DG_GEMM_KERNEL, FMT_44), , FMT_E4M3, FMT_E4M3)
 DG_GEMM_FORMATS(DG_KERNEL(DG_GEMM_KERNEL, FMT_55), _a5b5, FMT_E5M2, FMT_E5M2)
 DG_GEMM_FORMATS(DG_KERNEL(DG_GEMM_KERNEL, FMT_45), _a4b5, FMT_E4M3, FMT_E5M2)
