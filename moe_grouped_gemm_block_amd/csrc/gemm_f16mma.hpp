@@ -365,54 +365,101 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
     const uint8_t* la = lds + stage * A_BYTES;
     const uint8_t* lb = lds + 2 * A_BYTES + stage * B_BYTES;
 
-    // Raw FP8 fragments, all read before the first wait: A rows
-    // wm + 16 mi + r16 (the MFMA's second operand), bytes [32q, 32q+32), and
-    // the first two B column tiles.
-    int4 xa0[MI], xa1[MI];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      xa0[mi] = *reinterpret_cast<const int4*>(la + a_off0 + mi * 16 * KBLK);
-      xa1[mi] = *reinterpret_cast<const int4*>(la + a_off1 + mi * 16 * KBLK);
-    }
-    int4 y0 = *reinterpret_cast<const int4*>(lb + b_off0);
-    int4 y1 = *reinterpret_cast<const int4*>(lb + b_off1);
-    int4 z0 = y0, z1 = y1;
-    if (NI > 1) {
-      z0 = *reinterpret_cast<const int4*>(lb + b_off0 + 16 * KBLK);
-      z1 = *reinterpret_cast<const int4*>(lb + b_off1 + 16 * KBLK);
-    }
     v8h af[MI][4];
     v8h bf[4];
     v4f part[MI];
-    // Column tile 0, k-step by k-step: each A operand is converted just
-    // before its first MFMA, so the matrix core starts after a few
-    // conversions instead of after all of A.  The B operands of tile 1 are
-    // converted into the registers each k-step frees, and the raw bytes of
-    // tile 2 are read into those of tile 0.
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      bf[st] = fp8_operand<FB>(y0, y1, st);
+    int4 y0, y1;   // raw bytes of the B column tile after the next one
+    if constexpr (!ROW_SA) {
+      // Raw FP8 fragments, all read before the first wait: A rows
+      // wm + 16 mi + r16 (the MFMA's second operand), bytes [32q, 32q+32),
+      // and the first two B column tiles.
+      int4 xa0[MI], xa1[MI];
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
-        af[mi][st] = fp8_operand<FA>(xa0[mi], xa1[mi], st);
-        part[mi] = mfma16_f16(bf[st], af[mi][st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : part[mi]);
+        xa0[mi] = *reinterpret_cast<const int4*>(la + a_off0 + mi * 16 * KBLK);
+        xa1[mi] = *reinterpret_cast<const int4*>(la + a_off1 + mi * 16 * KBLK);
       }
+      y0 = *reinterpret_cast<const int4*>(lb + b_off0);
+      y1 = *reinterpret_cast<const int4*>(lb + b_off1);
+      int4 z0 = y0, z1 = y1;
       if (NI > 1) {
-        bf[st] = fp8_operand<FB>(z0, z1, st);
-        if (NI > 2 && st == 1) y0 = *reinterpret_cast<const int4*>(lb + b_off0 + 2 * 16 * KBLK);
-        if (NI > 2 && st == 3) y1 = *reinterpret_cast<const int4*>(lb + b_off1 + 2 * 16 * KBLK);
+        z0 = *reinterpret_cast<const int4*>(lb + b_off0 + 16 * KBLK);
+        z1 = *reinterpret_cast<const int4*>(lb + b_off1 + 16 * KBLK);
       }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * MI + (NI > 1 ? 4 : 2), 0);   // raw reads first
+      // Column tile 0, k-step by k-step: each A operand is converted just
+      // before its first MFMA, so the matrix core starts after a few
+      // conversions instead of after all of A.  The B operands of tile 1 are
+      // converted into the registers each k-step frees, and the raw bytes of
+      // tile 2 are read into those of tile 0.
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                       // B operand of tile 0
+      for (int st = 0; st < 4; ++st) {
+        bf[st] = fp8_operand<FB>(y0, y1, st);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          af[mi][st] = fp8_operand<FA>(xa0[mi], xa1[mi], st);
+          part[mi] = mfma16_f16(bf[st], af[mi][st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : part[mi]);
+        }
+        if (NI > 1) {
+          bf[st] = fp8_operand<FB>(z0, z1, st);
+          if (NI > 2 && st == 1) y0 = *reinterpret_cast<const int4*>(lb + b_off0 + 2 * 16 * KBLK);
+          if (NI > 2 && st == 3) y1 = *reinterpret_cast<const int4*>(lb + b_off1 + 2 * 16 * KBLK);
+        }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * MI + (NI > 1 ? 4 : 2), 0);   // raw reads first
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                     // B operand of tile 0
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                   // A operand
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // 1 MFMA
+        }
+        if (NI > 1) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);         // B operand of tile 1
+      }
+    } else {
+      // Row-scaled A: one more live register per row group, which leaves no
+      // room for the raw fragments of both operands at once (they would be
+      // spilled, and reloading a spill inside the loop waits for the copies
+      // in flight).  A is converted first, then tile 0 runs as the others do.
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                     // A operand
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // 1 MFMA
+        const int4 x0 = *reinterpret_cast<const int4*>(la + a_off0 + mi * 16 * KBLK);
+        const int4 x1 = *reinterpret_cast<const int4*>(la + a_off1 + mi * 16 * KBLK);
+        fp8x32_to_f16<FA>(x0, x1, af[mi]);
       }
-      if (NI > 1) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);           // B operand of tile 1
+      y0 = *reinterpret_cast<const int4*>(lb + b_off0);
+      y1 = *reinterpret_cast<const int4*>(lb + b_off1);
+      fp8x32_to_f16<FB>(y0, y1, bf);
+      if (NI > 1) {
+        y0 = *reinterpret_cast<const int4*>(lb + b_off0 + 16 * KBLK);
+        y1 = *reinterpret_cast<const int4*>(lb + b_off1 + 16 * KBLK);
+      }
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+          part[mi] = mfma16_f16(bf[st], af[mi][st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : part[mi]);
+        if (NI > 1) {
+          bf[st] = fp8_operand<FB>(y0, y1, st);   // operand st of tile 1
+          if (NI > 2 && st == 1) y0 = *reinterpret_cast<const int4*>(lb + b_off0 + 2 * 16 * KBLK);
+          if (NI > 2 && st == 3) y1 = *reinterpret_cast<const int4*>(lb + b_off1 + 2 * 16 * KBLK);
+        }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      if (NI > 1) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          if (st > 0) {
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+              __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // 1 VALU (convert)
+            }
+          } else {
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);     // converts of operand 0
+          }
+        }
+      }
     }
     // Column tiles 1 .. NI-1, software-pipelined: while the MFMAs of tile ni
     // consume operand st, operand st of tile ni+1 is converted into the
