@@ -15,9 +15,9 @@ region (TFLOP/s of algorithmic work = 2 * real_rows * N * K, or GB/s of
 algorithmic bytes for the memory-bound skinny shape).  `roofline.achieved`
 uses the kernel's average duration from HIP events recorded on the launch
 stream around the timed steps.  `kernel_ms_eager` is the same kernel timed
-with launches one by one after the timed region: rocprofv3's kernel trace
-reports that duration per dispatch (graph-launched ones included), so it is
-the figure that the committed profile summaries agree with.
+with launches one by one after the timed region, for comparison with the
+per-dispatch durations of a kernel trace (the committed profile summaries
+list the profiled and the unprofiled figures side by side).
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload
 on this host.
 
@@ -212,10 +212,9 @@ def run_timed(step, K: int, W: int, use_graph: bool):
 
 def eager_kernel_ms(step, K: int, use_graph: bool):
     """Per-launch kernel time with the steps launched one by one (HIP events
-    on the launch stream), measured after the timed region.  This is the
-    duration rocprofv3's kernel trace reports per dispatch, also for
-    graph-launched kernels, so it is the figure to compare with the committed
-    profile summaries.  None when the timed region itself was eager."""
+    on the launch stream), measured after the timed region: the launch mode
+    of a kernel trace's per-dispatch durations.  None when the timed region
+    itself was eager."""
     if not use_graph:
         return None
     _, ms, _ = run_timed(step, min(K, 50), 5, False)
