@@ -49,7 +49,7 @@ int check_common(const void* A, const float* sA, const void* B, const float* sB,
 // Tile shape of one launch.  Every wave owns a 64 x 128 sub-tile, except in
 // the 8-wave 128 x 256 tile (64 x 64).  The 128 x 512 tile runs 8 waves (two
 // per SIMD, one workgroup per CU, 160 KB of LDS); the 128 x 256 tile runs 4
-// or 8 waves (see launch_256), serves narrow problems and finishes the last
+// or 8 waves (see launch_narrow), serves narrow problems and finishes the last
 // partial round of a large problem (see launch()); the 128 x 128
 // tile (2 waves, 64 KB of LDS) is the alternative for that last round.  The
 // 256 x 256 tile (8 waves, 128 KB of LDS) computes bit-identical results to
@@ -58,9 +58,10 @@ int check_common(const void* A, const float* sA, const void* B, const float* sB,
 // DG_FORCE_TILE=512, 256 or 128 uses that tile for every problem (few rows
 // included), 2256 the 256 x 256 tile for every dense problem, 1512 selects
 // the 1 x 8 wave arrangement where it applies, 8256 the 8-wave 128 x 256
-// tile wherever a 128 x 256 tile is used (256: the 4-wave one);
+// tile wherever a 128 x 256 tile is used (256: the 4-wave one), 4128 the
+// 4-wave 128 x 128 tile of 64 x 64 waves there;
 // DG_TAIL_TILE=0 / 128 / 256 / 8256 switches off or sets the tile of the
-// last partial round (256: 128 x 256, 4 or 8 waves as launch_256 picks;
+// last partial round (256: 128 x 256, 4 or 8 waves as launch_narrow picks;
 // 8256: always 8 waves) (tuning aids).
 constexpr int kCUs = 256;
 
@@ -130,13 +131,15 @@ typedef void (*kfn)(dg::GemmArgs);
 
 // Kernels of one pair of operand formats; combo = 2 * a_fmt + b_fmt.  The
 // *rs kernels take one A scale per row (1 x 128 blocks).
-struct TiledSet { kfn k512[2], k256[2], k128[2], k256sq[2], k256w8[2]; };   // [f32, bf16]
+struct TiledSet { kfn k512[2], k256[2], k128[2], k256sq[2], k256w8[2], k128w4[2], k64w2[2]; };   // [f32, bf16]
 #define DG_TILED_SET(SFX)                                                   \
   {{dg::dg_gemm_128x512_f32##SFX, dg::dg_gemm_128x512_bf16##SFX},           \
    {dg::dg_gemm_128x256_f32##SFX, dg::dg_gemm_128x256_bf16##SFX},           \
    {dg::dg_gemm_128x128_f32##SFX, dg::dg_gemm_128x128_bf16##SFX},           \
    {dg::dg_gemm_256x256_f32##SFX, dg::dg_gemm_256x256_bf16##SFX},           \
-   {dg::dg_gemm_128x256w8_f32##SFX, dg::dg_gemm_128x256w8_bf16##SFX}}
+   {dg::dg_gemm_128x256w8_f32##SFX, dg::dg_gemm_128x256w8_bf16##SFX},       \
+   {dg::dg_gemm_128x128w4_f32##SFX, dg::dg_gemm_128x128w4_bf16##SFX},       \
+   {dg::dg_gemm_128x64w2_f32##SFX, dg::dg_gemm_128x64w2_bf16##SFX}}
 // [A scales per 128 x 128 block / per row][combo]
 const TiledSet kTiled[2][4] = {
     {DG_TILED_SET(), DG_TILED_SET(_a4b5), DG_TILED_SET(_a5b4), DG_TILED_SET(_a5b5)},
@@ -196,19 +199,52 @@ int launch_segments(dg::GemmArgs a, int out_dtype, int combo, hipStream_t stream
   return err == hipSuccess ? DG_OK : DG_ERR_LAUNCH;
 }
 
-// 128 x 256 tiles over the row tiles [m_tile0, m_tile0 + m_tiles) (all when
-// m_tiles < 0).  With at most half as many workgroups as CUs every tile runs
-// alone on its CU and its latency is the launch's time: the 8-wave tile
-// (64 x 64 per wave, two waves per SIMD) finishes it sooner.  With more
-// workgroups the chip runs at its power limit and the 4-wave tile's fewer
-// conversions per MFMA (1.5 instead of 2) win.
-int launch_256(const dg::GemmArgs& a, const TiledSet& ks, int out_dtype, hipStream_t stream, int m_tile0 = 0,
-               int m_tiles = -1) {
+// Tiles of 128 rows and at most 256 columns.  A launch whose workgroups all
+// run at once takes about one tile's time, so what counts is rounds of
+// workgroups (one per CU) times the time of one tile.  Per-tile times
+// relative to the 8-wave 128 x 512 tile, measured on the MI355X at
+// K = 4096 with one workgroup per CU:
+//   128 x 256,  4 waves of 64 x 128   0.74
+//   128 x 256,  8 waves of 64 x 64    0.69 while at most 3/4 of the CUs are
+//                                     busy, 0.78 beyond (the chip then runs
+//                                     at its power limit, and this tile
+//                                     converts 2 values per MFMA, not 1.5)
+//   128 x 128,  4 waves of 64 x 64    0.40
+//   128 x  64,  2 waves of 64 x 64    0.38
+enum NarrowTile { kN256w4 = 0, kN256w8, kN128w4, kN64w2, kNarrowTiles };
+
+int64_t rounds(int64_t wgs) { return (wgs + kCUs - 1) / kCUs; }
+
+double narrow_time(int t, int64_t rows, int64_t N) {
+  const int64_t wgs = rows * ((N + (t == kN64w2 ? 63 : t == kN128w4 ? 127 : 255)) / (t == kN64w2 ? 64 : t == kN128w4 ? 128 : 256));
+  const double per = t == kN256w4 ? 0.74 : t == kN256w8 ? (wgs <= 3 * kCUs / 4 ? 0.69 : 0.78) : t == kN128w4 ? 0.40 : 0.38;
+  return double(rounds(wgs)) * per;
+}
+
+int best_narrow(int64_t rows, int64_t N, double* est = nullptr) {
+  int best = kN256w4;
+  for (int t = kN256w4 + 1; t < kNarrowTiles; ++t)
+    if (narrow_time(t, rows, N) < narrow_time(best, rows, N)) best = t;
+  if (est) *est = narrow_time(best, rows, N);
+  return best;
+}
+
+// The row tiles [m_tile0, m_tile0 + m_tiles) (all when m_tiles < 0) on the
+// narrow tile with the least estimated time (or the one an override names).
+int launch_narrow(const dg::GemmArgs& a, const TiledSet& ks, int out_dtype, hipStream_t stream, int m_tile0 = 0,
+                  int m_tiles = -1) {
   const int64_t rows = m_tiles >= 0 ? m_tiles : (int64_t(a.M) + 127) / 128;
-  const int64_t blocks = rows * ((int64_t(a.N) + 255) / 256);
-  if (forced_tile() == 8256 || tail_tile() == 8256 || (forced_tile() != 256 && blocks <= kCUs / 2))
-    return launch_tiles(a, 256, 512, ks.k256w8[1], ks.k256w8[0], out_dtype, stream, m_tile0, m_tiles);
-  return launch_tiles(a, 256, 256, ks.k256[1], ks.k256[0], out_dtype, stream, m_tile0, m_tiles);
+  int t = best_narrow(rows, a.N);
+  if (forced_tile() == 256) t = kN256w4;
+  if (forced_tile() == 8256 || tail_tile() == 8256) t = kN256w8;
+  if (forced_tile() == 4128) t = kN128w4;
+  if (forced_tile() == 264) t = kN64w2;
+  switch (t) {
+    case kN64w2: return launch_tiles(a, 64, 128, ks.k64w2[1], ks.k64w2[0], out_dtype, stream, m_tile0, m_tiles);
+    case kN128w4: return launch_tiles(a, 128, 256, ks.k128w4[1], ks.k128w4[0], out_dtype, stream, m_tile0, m_tiles);
+    case kN256w8: return launch_tiles(a, 256, 512, ks.k256w8[1], ks.k256w8[0], out_dtype, stream, m_tile0, m_tiles);
+    default: return launch_tiles(a, 256, 256, ks.k256[1], ks.k256[0], out_dtype, stream, m_tile0, m_tiles);
+  }
 }
 
 int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, int row_sa, hipStream_t stream) {
@@ -219,6 +255,12 @@ int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, int row_s
   const int64_t m_tiles = (int64_t(a.M) + 127) / 128;
   const int64_t wide = m_tiles * ((int64_t(a.N) + 511) / 512);
   bool use512 = a.N > 256 && wide >= kCUs / 2;
+  if (use512 && wide < kCUs) {
+    // less than one round of 128 x 512 tiles: narrower tiles may fill more CUs
+    double narrow = 0.0;
+    best_narrow(m_tiles, a.N, &narrow);
+    if (narrow < 1.0) use512 = false;
+  }
   if (forced_tile() == 512) use512 = true;
   if (forced_tile() == 256) use512 = false;
   // the 1 x 8 variant exists for E4M3 x E4M3 without K or N tails
@@ -226,7 +268,7 @@ int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, int row_s
     return launch_tiles(a, 512, 512, dg::dg_gemm_wide_128x512_bf16, dg::dg_gemm_wide_128x512_f32, out_dtype,
                         stream);
   if (forced_tile() == 128) return launch_tiles(a, 128, 128, ks.k128[1], ks.k128[0], out_dtype, stream);
-  if (forced_tile() == 8256) return launch_256(a, ks, out_dtype, stream);
+  if (forced_tile() == 8256 || forced_tile() == 4128 || forced_tile() == 264) return launch_narrow(a, ks, out_dtype, stream);
   if (a.offs == nullptr) {
     const int64_t m256 = (int64_t(a.M) + 255) / 256, t256 = m256 * ((int64_t(a.N) + 255) / 256);
     if (forced_tile() == 2256 || (forced_tile() == 0 && a.M % 256 == 0 && t256 % kCUs == 0))
@@ -248,11 +290,11 @@ int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, int row_s
       const int rest = int(m_tiles - main_m);
       if (tail_tile() == 128)
         return launch_tiles(a, 128, 128, ks.k128[1], ks.k128[0], out_dtype, stream, int(main_m), rest);
-      return launch_256(a, ks, out_dtype, stream, int(main_m), rest);
+      return launch_narrow(a, ks, out_dtype, stream, int(main_m), rest);
     }
   }
   if (use512) return launch_tiles(a, 512, 512, ks.k512[1], ks.k512[0], out_dtype, stream);
-  return launch_256(a, ks, out_dtype, stream);
+  return launch_narrow(a, ks, out_dtype, stream);
 }
 
 bool valid_fmt(int f) { return f == DG_FP8_E4M3 || f == DG_FP8_E5M2; }

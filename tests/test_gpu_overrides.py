@@ -17,6 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 @pytest.mark.parametrize("env", [{"DG_FORCE_TILE": "1512"}, {"DG_FORCE_TILE": "512"},
                                  {"DG_FORCE_TILE": "2256"}, {"DG_FORCE_TILE": "8256"},
+                                 {"DG_FORCE_TILE": "4128"}, {"DG_FORCE_TILE": "264"},
                                  {"DG_TAIL_TILE": "8256"},
                                  {"DG_FORCE_TILE": "256"}, {"DG_FORCE_TILE": "128"},
                                  {"DG_TAIL_TILE": "0"}, {"DG_TAIL_TILE": "128"}],
