@@ -126,12 +126,10 @@ def test_e5m2_subnormal_operands():
     check(C.cpu().numpy().astype(np.float64), Cr, mass, "f32", "e5m2 subnormals")
 
 
-def test_full_size_e5m2_sampled():
-    log("e5m2 4096^3 bf16 sampled")
+def test_full_size_e5m2_full():
+    log("e5m2 4096^3 bf16, every output")
     p = I.dense_problem(4096, 4096, 4096, seed=2, out_dtype="bf16", block_log2_range=4.0,
                         a_fmt="e5m2", b_fmt="e5m2")
     Cg = run_dense(p)
-    rng = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([rng.integers(0, 4096, 32), [0, 127, 128, 4095]]))
-    Cr, mass = oracle.gemm_blockscaled(p.A, p.sA, p.B, p.sB, rows=rows, a_fmt="e5m2", b_fmt="e5m2")
-    check(Cg[rows], Cr, mass, "bf16", "4096^3 e5m2")
+    Cr, mass = oracle.gemm_blockscaled(p.A, p.sA, p.B, p.sB, a_fmt="e5m2", b_fmt="e5m2")
+    check(Cg, Cr, mass, "bf16", "4096^3 e5m2")
