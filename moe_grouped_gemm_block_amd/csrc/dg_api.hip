@@ -46,23 +46,23 @@ int check_common(const void* A, const float* sA, const void* B, const float* sB,
   return DG_OK;
 }
 
-// Tile shape of one launch.  Every wave owns a 64 x 128 sub-tile, except in
-// the 8-wave 128 x 256 tile (64 x 64).  The 128 x 512 tile runs 8 waves (two
-// per SIMD, one workgroup per CU, 160 KB of LDS); the 128 x 256 tile runs 4
-// or 8 waves (see launch_narrow), serves narrow problems and finishes the last
-// partial round of a large problem (see launch()); the 128 x 128
-// tile (2 waves, 64 KB of LDS) is the alternative for that last round.  The
-// 256 x 256 tile (8 waves, 128 KB of LDS) computes bit-identical results to
-// 128 x 512 and copies 20 % fewer bytes per K-block; it takes dense problems
+// Tile shape of one launch.  The 128 x 512 tile runs 8 waves of 64 x 128
+// (two per SIMD, one workgroup per CU, 160 KB of LDS); the 256 x 256 tile
+// (8 waves of 64 x 128, 128 KB of LDS) computes bit-identical results to
+// 128 x 512, copies 20 % fewer bytes per K-block and takes dense problems
 // whose 256 x 256 tiles fill whole rounds of the CUs (4096^3, 8192^2 x K, ...).
+// Narrow problems and the last partial round of a large one run on the
+// narrow tiles chosen by launch_narrow: 128 x 256 (4 waves of 64 x 128 or 8
+// of 64 x 64), 128 x 128 (4 waves of 64 x 64) or 128 x 64 (2 waves of
+// 64 x 64).  The 128 x 128 tile of 2 waves of 64 x 128 (64 KB of LDS) is a
+// tuning alternative for the last round.
 // DG_FORCE_TILE=512, 256 or 128 uses that tile for every problem (few rows
 // included), 2256 the 256 x 256 tile for every dense problem, 1512 selects
-// the 1 x 8 wave arrangement where it applies, 8256 the 8-wave 128 x 256
-// tile wherever a 128 x 256 tile is used (256: the 4-wave one), 4128 the
-// 4-wave 128 x 128 tile of 64 x 64 waves there;
-// DG_TAIL_TILE=0 / 128 / 256 / 8256 switches off or sets the tile of the
-// last partial round (256: 128 x 256, 4 or 8 waves as launch_narrow picks;
-// 8256: always 8 waves) (tuning aids).
+// the 1 x 8 wave arrangement where it applies, and 8256 / 4128 / 264 the
+// 8-wave 128 x 256 / 4-wave 128 x 128 / 2-wave 128 x 64 tile wherever a
+// narrow tile is used; DG_TAIL_TILE=0 / 128 / 256 / 8256 switches off the
+// separate last round or sets its tile (256: launch_narrow's choice; 8256:
+// the 8-wave 128 x 256 tile) (tuning aids).
 constexpr int kCUs = 256;
 
 int forced_tile() {
