@@ -1,4 +1,4 @@
-"""Seeded random shapes through the automatic tile choice (the host picks
+"""Seeded random dense and grouped shapes through the automatic tile choice (the host picks
 among seven tile shapes from M, N and the CU count, and may split a grid
 into a main launch and a last-round launch), each compared with the CPU
 oracle to the parity bound.  Rows are sampled for the larger shapes, always
@@ -56,3 +56,43 @@ def test_random_dense(M, N, K, out):
     ratio = float((np.abs(Cg - Cr) / bound).max())
     log(f"  random {M}x{N}x{K} {out}: max err/bound = {ratio:.3g}")
     assert np.all(np.isfinite(Cg)) and ratio <= 1.0
+
+
+def grouped_cases(n=10, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        G = int(rng.integers(1, 12))
+        counts = [int(c) if rng.random() > 0.2 else 0 for c in rng.integers(1, 700, G)]
+        N = int(rng.choice([rng.integers(8, 600), rng.integers(600, 3000)]))
+        K = int(16 * rng.integers(1, 24))
+        out.append((tuple(counts), N, K, "bf16" if i % 2 else "f32"))
+    return out
+
+
+@pytest.mark.parametrize("counts,N,K,out", grouped_cases())
+def test_random_grouped(counts, N, K, out):
+    """Experts with random row counts (some empty), each segment padded to a
+    multiple of 128 rows with zero rows; padding rows must come out zero."""
+    rng = np.random.default_rng(sum(counts) + N + K)
+    G = len(counts)
+    offs = np.concatenate([[0], np.cumsum([-(-c // 128) * 128 for c in counts])]).astype(np.int32)
+    A = np.zeros((int(offs[-1]), K), np.float32)
+    for e, c in enumerate(counts):
+        A[offs[e]:offs[e] + c] = rng.standard_normal((c, K), dtype=np.float32)
+    qA, sA = I.quantize(A)
+    Kb = -(-K // 128)
+    qB = np.empty((G, N, K), np.uint8)
+    sB = np.empty((G, -(-N // 128), Kb), np.float32)
+    for e in range(G):
+        qB[e], sB[e] = I.quantize(rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02))
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    C = dg.grouped_gemm_fp8(t(qA), t(sA), t(qB), t(sB), t(offs), out)
+    torch.cuda.synchronize()
+    Cg = C.float().cpu().numpy().astype(np.float64)
+    Cr, mass = oracle.grouped_gemm(qA, sA, qB, sB, offs)
+    ratio = float((np.abs(Cg - Cr) / oracle.tolerance(Cr, mass, out)).max()) if Cg.size else 0.0
+    log(f"  random grouped G={G} rows={int(offs[-1])} N={N} K={K} {out}: max err/bound = {ratio:.3g}")
+    assert np.all(np.isfinite(Cg)) and ratio <= 1.0
+    for e, c in enumerate(counts):
+        assert np.all(Cg[offs[e] + c:offs[e + 1]] == 0)
