@@ -213,14 +213,24 @@ int launch_segments(dg::GemmArgs a, int out_dtype, int combo, hipStream_t stream
 //   128 x  64,  2 waves of 64 x 64    0.38
 enum NarrowTile { kN256w4 = 0, kN256w8, kN128w4, kN64w2, kNarrowTiles };
 
+struct NarrowShape {
+  int cols;          // tile width
+  double t;          // per-tile time relative to 128 x 512
+  double t_crowded;  // the same once more than 3/4 of the CUs hold a tile
+};
+constexpr NarrowShape kNarrow[kNarrowTiles] = {
+    {256, 0.74, 0.74}, {256, 0.69, 0.78}, {128, 0.40, 0.40}, {64, 0.38, 0.38}};
+
 int64_t rounds(int64_t wgs) { return (wgs + kCUs - 1) / kCUs; }
 
+// Estimated time of `rows` row tiles x N columns on narrow tile t.
 double narrow_time(int t, int64_t rows, int64_t N) {
-  const int64_t wgs = rows * ((N + (t == kN64w2 ? 63 : t == kN128w4 ? 127 : 255)) / (t == kN64w2 ? 64 : t == kN128w4 ? 128 : 256));
-  const double per = t == kN256w4 ? 0.74 : t == kN256w8 ? (wgs <= 3 * kCUs / 4 ? 0.69 : 0.78) : t == kN128w4 ? 0.40 : 0.38;
-  return double(rounds(wgs)) * per;
+  const NarrowShape& n = kNarrow[t];
+  const int64_t wgs = rows * ((N + n.cols - 1) / n.cols);
+  return double(rounds(wgs)) * (wgs <= 3 * kCUs / 4 ? n.t : n.t_crowded);
 }
 
+// The narrow tile with the least estimated time (ties go to the wider tile).
 int best_narrow(int64_t rows, int64_t N, double* est = nullptr) {
   int best = kN256w4;
   for (int t = kN256w4 + 1; t < kNarrowTiles; ++t)
