@@ -225,33 +225,51 @@ def bench_torch_matmul(args):
     """The vendor library's plain GEMM on the same shape, for comparison:
     torch.matmul on BF16 (or FP16) operands, which runs hipBLASLt.  No FP8
     decode, no block scales: a reference point for the matrix cores' rate,
-    not the block-scaled operation."""
+    not the block-scaled operation.  --dtype fp8: torch._scaled_mm on E4M3
+    operands with one scale per tensor (FP8 matrix cores, BF16 out), the
+    vendor's FP8 rate; its FP8 accumulation is not held to this library's
+    tolerance and it has no block scales."""
     import torch
     dev = torch.device("cuda:0")
-    dt = torch.bfloat16 if args.dtype == "bf16" else torch.float16
     M = N = K = 4096
     gen = torch.Generator(device="cpu").manual_seed(2)
     R = args.rotate or 8
-    ops = [(torch.randn(M, K, generator=gen).to(dt).to(dev),
-            torch.randn(K, N, generator=gen).to(dt).to(dev).t().contiguous().t(),   # stored N x K, as B
-            torch.empty(M, N, dtype=dt, device=dev)) for _ in range(R)]
+    if args.dtype == "fp8":
+        f8 = torch.float8_e4m3fn
+        one = torch.ones((), dtype=torch.float32, device=dev)
+        ops = [(torch.randn(M, K, generator=gen).to(dev).to(f8),
+                torch.randn(N, K, generator=gen).to(dev).to(f8).t(),          # stored N x K, column-major B
+                torch.empty(M, N, dtype=torch.bfloat16, device=dev)) for _ in range(R)]
 
-    def step(i, sh):                 # torch enqueues on its current stream, which is sh here
-        a, b, c = ops[i % R]
-        torch.matmul(a, b, out=c)
+        def step(i, sh):
+            a, b, c = ops[i % R]
+            torch._scaled_mm(a, b, scale_a=one, scale_b=one, out_dtype=torch.bfloat16, out=c)
+    else:
+        dt = torch.bfloat16 if args.dtype == "bf16" else torch.float16
+        ops = [(torch.randn(M, K, generator=gen).to(dt).to(dev),
+                torch.randn(K, N, generator=gen).to(dt).to(dev).t().contiguous().t(),   # stored N x K, as B
+                torch.empty(M, N, dtype=dt, device=dev)) for _ in range(R)]
+
+        def step(i, sh):                 # torch enqueues on its current stream, which is sh here
+            a, b, c = ops[i % R]
+            torch.matmul(a, b, out=c)
 
     ms_step, kern_ms, _ = run_timed(step, args.steps, args.warmup, not args.no_graph)
     flop = 2.0 * M * N * K
     achieved = flop / (kern_ms * 1e-3) / 1e12
-    line = {"metric": f"vendor {args.dtype.upper()} GEMM TFLOPS (torch.matmul / hipBLASLt), same shape, for comparison",
+    api = "torch._scaled_mm, one scale per tensor" if args.dtype == "fp8" else "torch.matmul"
+    line = {"metric": f"vendor {args.dtype.upper()} GEMM TFLOPS ({api} / hipBLASLt), same shape, for comparison",
             "value": round(flop / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.dtype,
             "data": "synthetic",
             "config": {"workload": f"torch_matmul_4096_{args.dtype}", "M": M, "N": N, "K": K,
                        "operand_copies": R, "launch": "eager" if args.no_graph else "hip_graph"},
-            "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": None},
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
+                         "peak": PEAK_FP8_TFLOPS if args.dtype == "fp8" else PEAK_FP16_TFLOPS,
+                         "unit": "TFLOP/s",
+                         "frac": round(achieved / (PEAK_FP8_TFLOPS if args.dtype == "fp8" else PEAK_FP16_TFLOPS), 4),
+                         "traffic": None},
             "cpu_baseline": None, "kernel_ms": round(kern_ms, 5)}
     print(json.dumps(line), flush=True)
 
@@ -320,7 +338,7 @@ def main():
                     help="launch the timed steps one by one from Python instead of replaying a HIP graph")
     ap.add_argument("--op", choices=["gemm", "quantize", "torch-matmul"], default="gemm",
                     help="torch-matmul: the vendor BF16/FP16 GEMM on 4096^3, for comparison")
-    ap.add_argument("--dtype", choices=["bf16", "fp16"], default="bf16", help="operand type of --op torch-matmul")
+    ap.add_argument("--dtype", choices=["bf16", "fp16", "fp8"], default="bf16", help="operand type of --op torch-matmul")
     ap.add_argument("--a-scale", choices=["128x128", "1x128"], default="128x128",
                     help="A scale blocks of the GEMM: 128x128, or one per token and 128 columns")
     ap.add_argument("--fmt", choices=["e4m3", "e5m2"], default="e4m3",
