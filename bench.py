@@ -33,7 +33,9 @@ Workloads (seeded, synthetic; see inputs.make_config):
 --op quantize times the activation quantisation that produces A instead
 (4096 x 4096 BF16 in, E4M3 codes and FP32 block scales out; HBM-bound).
 --op torch-matmul times the vendor library's plain BF16 (or FP16) GEMM,
-torch.matmul on 4096^3, as a reference point for the matrix cores' rate.
+torch.matmul on 4096^3, as a reference point for the matrix cores' rate;
+--dtype fp8 its FP8 GEMM (torch._scaled_mm, one scale per tensor, FP8
+matrix cores).
 """
 from __future__ import annotations
 
