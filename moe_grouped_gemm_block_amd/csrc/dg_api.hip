@@ -10,12 +10,11 @@
 #include <vector>
 
 #include "dg.h"
-// this translation unit defines the 1 x 8-wave variant and the quantiser; the
-// GEMM kernels of each operand-format pair are defined in kernels_*.hip
+// this translation unit defines the quantiser; the GEMM kernels of each
+// operand-format pair are defined in kernels_*.hip
 #define DG_DEFINE_MISC
 #include "gemm_f16mma.hpp"
 #include "gemm_skinny.hpp"
-#include "gemm_wide.hpp"
 #include "quant.hpp"
 
 namespace {
@@ -54,16 +53,27 @@ int check_common(const void* A, const float* sA, const void* B, const float* sB,
 // Narrow problems and the last partial round of a large one run on the
 // narrow tiles chosen by launch_narrow: 128 x 256 (4 waves of 64 x 128 or 8
 // of 64 x 64), 128 x 128 (4 waves of 64 x 64) or 128 x 64 (2 waves of
-// 64 x 64).  The 128 x 128 tile of 2 waves of 64 x 128 (64 KB of LDS) is a
-// tuning alternative for the last round.
-// DG_FORCE_TILE=512, 256 or 128 uses that tile for every problem (few rows
-// included), 2256 the 256 x 256 tile for every dense problem, 1512 selects
-// the 1 x 8 wave arrangement where it applies, and 8256 / 4128 / 264 the
-// 8-wave 128 x 256 / 4-wave 128 x 128 / 2-wave 128 x 64 tile wherever a
-// narrow tile is used; DG_TAIL_TILE=0 / 128 / 256 / 8256 switches off the
-// separate last round or sets its tile (256: launch_narrow's choice; 8256:
-// the 8-wave 128 x 256 tile) (tuning aids).
-constexpr int kCUs = 256;
+// 64 x 64).
+// DG_FORCE_TILE=512 or 256 uses that tile for every problem (few rows
+// included), 2256 the 256 x 256 tile for every dense problem, and 8256 /
+// 4128 / 264 the 8-wave 128 x 256 / 4-wave 128 x 128 / 2-wave 128 x 64 tile
+// wherever a narrow tile is used; DG_TAIL_TILE=0 / 256 / 8256 switches off
+// the separate last round or sets its tile (256: launch_narrow's choice;
+// 8256: the 8-wave 128 x 256 tile) (tuning aids).
+
+// Compute units of the current device (one workgroup of the tiled kernels
+// fills one), queried once per device and cached; 256 on the MI355X.
+int num_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
 
 int forced_tile() {
   static const int v = [] {
@@ -131,11 +141,10 @@ typedef void (*kfn)(dg::GemmArgs);
 
 // Kernels of one pair of operand formats; combo = 2 * a_fmt + b_fmt.  The
 // *rs kernels take one A scale per row (1 x 128 blocks).
-struct TiledSet { kfn k512[2], k256[2], k128[2], k256sq[2], k256w8[2], k128w4[2], k64w2[2]; };   // [f32, bf16]
+struct TiledSet { kfn k512[2], k256[2], k256sq[2], k256w8[2], k128w4[2], k64w2[2]; };   // [f32, bf16]
 #define DG_TILED_SET(SFX)                                                   \
   {{dg::dg_gemm_128x512_f32##SFX, dg::dg_gemm_128x512_bf16##SFX},           \
    {dg::dg_gemm_128x256_f32##SFX, dg::dg_gemm_128x256_bf16##SFX},           \
-   {dg::dg_gemm_128x128_f32##SFX, dg::dg_gemm_128x128_bf16##SFX},           \
    {dg::dg_gemm_256x256_f32##SFX, dg::dg_gemm_256x256_bf16##SFX},           \
    {dg::dg_gemm_128x256w8_f32##SFX, dg::dg_gemm_128x256w8_bf16##SFX},       \
    {dg::dg_gemm_128x128w4_f32##SFX, dg::dg_gemm_128x128w4_bf16##SFX},       \
@@ -164,7 +173,7 @@ const SkinnySet kSkinny[4] = {DG_SKINNY_SET(), DG_SKINNY_SET(_a4b5), DG_SKINNY_S
 // splitting K; NI = 3 once that still gives every CU a workgroup.
 int launch_skinny(dg::GemmArgs a, int out_dtype, int combo, int row_sa, hipStream_t stream) {
   const int rows = a.M <= 16 ? 0 : a.M <= 32 ? 1 : 2;
-  const int wide = int64_t(a.N) >= int64_t(48) * kCUs ? 1 : 0;
+  const int wide = int64_t(a.N) >= int64_t(48) * num_cus() ? 1 : 0;
   const int cols = wide ? 48 : 16;
   const int64_t blocks = (int64_t(a.N) + cols - 1) / cols;
   if (blocks > INT32_MAX) return DG_ERR_UNSUPPORTED;
@@ -187,7 +196,7 @@ const SegSet kSeg[4] = {DG_SEG_SET(), DG_SEG_SET(_a4b5), DG_SEG_SET(_a5b4), DG_S
 // per expert.  The slab width is 48 once that still gives every CU a
 // workgroup.
 int launch_segments(dg::GemmArgs a, int out_dtype, int combo, hipStream_t stream) {
-  const int wide = int64_t(a.G) * ((int64_t(a.N) + 47) / 48) >= kCUs ? 1 : 0;
+  const int wide = int64_t(a.G) * ((int64_t(a.N) + 47) / 48) >= num_cus() ? 1 : 0;
   const int cols = wide ? 48 : 16;
   const int64_t slabs = (int64_t(a.N) + cols - 1) / cols;
   const int64_t blocks = slabs * a.G;
@@ -221,13 +230,13 @@ struct NarrowShape {
 constexpr NarrowShape kNarrow[kNarrowTiles] = {
     {256, 0.74, 0.74}, {256, 0.69, 0.78}, {128, 0.40, 0.40}, {64, 0.38, 0.38}};
 
-int64_t rounds(int64_t wgs) { return (wgs + kCUs - 1) / kCUs; }
+int64_t rounds(int64_t wgs) { return (wgs + num_cus() - 1) / num_cus(); }
 
 // Estimated time of `rows` row tiles x N columns on narrow tile t.
 double narrow_time(int t, int64_t rows, int64_t N) {
   const NarrowShape& n = kNarrow[t];
   const int64_t wgs = rows * ((N + n.cols - 1) / n.cols);
-  return double(rounds(wgs)) * (wgs <= 3 * kCUs / 4 ? n.t : n.t_crowded);
+  return double(rounds(wgs)) * (wgs <= 3 * num_cus() / 4 ? n.t : n.t_crowded);
 }
 
 // The narrow tile with the least estimated time (ties go to the wider tile).
@@ -264,8 +273,8 @@ int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, int row_s
     return launch_skinny(a, out_dtype, combo, row_sa, stream);
   const int64_t m_tiles = (int64_t(a.M) + 127) / 128;
   const int64_t wide = m_tiles * ((int64_t(a.N) + 511) / 512);
-  bool use512 = a.N > 256 && wide >= kCUs / 2;
-  if (use512 && wide < kCUs) {
+  bool use512 = a.N > 256 && wide >= num_cus() / 2;
+  if (use512 && wide < num_cus()) {
     // less than one round of 128 x 512 tiles: narrower tiles may fill more CUs
     double narrow = 0.0;
     best_narrow(m_tiles, a.N, &narrow);
@@ -273,15 +282,10 @@ int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, int row_s
   }
   if (forced_tile() == 512) use512 = true;
   if (forced_tile() == 256) use512 = false;
-  // the 1 x 8 variant exists for E4M3 x E4M3 without K or N tails
-  if (forced_tile() == 1512 && combo == 0 && !row_sa && a.K % dg::KBLK == 0 && a.N % 8 == 0)
-    return launch_tiles(a, 512, 512, dg::dg_gemm_wide_128x512_bf16, dg::dg_gemm_wide_128x512_f32, out_dtype,
-                        stream);
-  if (forced_tile() == 128) return launch_tiles(a, 128, 128, ks.k128[1], ks.k128[0], out_dtype, stream);
   if (forced_tile() == 8256 || forced_tile() == 4128 || forced_tile() == 264) return launch_narrow(a, ks, out_dtype, stream);
   if (a.offs == nullptr) {
     const int64_t m256 = (int64_t(a.M) + 255) / 256, t256 = m256 * ((int64_t(a.N) + 255) / 256);
-    if (forced_tile() == 2256 || (forced_tile() == 0 && a.M % 256 == 0 && t256 % kCUs == 0))
+    if (forced_tile() == 2256 || (forced_tile() == 0 && a.M % 256 == 0 && t256 % num_cus() == 0))
       return launch_tiles(a, 256, 512, ks.k256sq[1], ks.k256sq[0], out_dtype, stream, 0, int(m256));
   }
   if (use512 && forced_tile() == 0 && tail_tile() != 0) {
@@ -293,13 +297,11 @@ int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, int row_s
     // tile is still computed whole by one workgroup).
     const int64_t nt = (int64_t(a.N) + 511) / 512;
     const int64_t T = m_tiles * nt;
-    const int64_t main_m = (T / kCUs) * kCUs / nt;
-    if (T % kCUs != 0 && main_m > 0 && main_m < m_tiles) {
+    const int64_t main_m = (T / num_cus()) * num_cus() / nt;
+    if (T % num_cus() != 0 && main_m > 0 && main_m < m_tiles) {
       int st = launch_tiles(a, 512, 512, ks.k512[1], ks.k512[0], out_dtype, stream, 0, int(main_m));
       if (st != DG_OK) return st;
       const int rest = int(m_tiles - main_m);
-      if (tail_tile() == 128)
-        return launch_tiles(a, 128, 128, ks.k128[1], ks.k128[0], out_dtype, stream, int(main_m), rest);
       return launch_narrow(a, ks, out_dtype, stream, int(main_m), rest);
     }
   }

@@ -562,14 +562,12 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   DG_GEMM_SHAPE(K, 256x256, 4, 2, 128, SFX, FA, FB, false)                  \
   DG_GEMM_SHAPE(K, 128x256, 2, 2, 128, SFX, FA, FB, false)                  \
   DG_GEMM_SHAPE(K, 128x256w8, 2, 4, 64, SFX, FA, FB, false)                 \
-  DG_GEMM_SHAPE(K, 128x128, 2, 1, 128, SFX, FA, FB, false)                  \
   DG_GEMM_SHAPE(K, 128x128w4, 2, 2, 64, SFX, FA, FB, false)                 \
   DG_GEMM_SHAPE(K, 128x64w2, 2, 1, 64, SFX, FA, FB, false)                  \
   DG_GEMM_SHAPE(K, 128x512, 2, 4, 128, SFX##_rs, FA, FB, true)              \
   DG_GEMM_SHAPE(K, 256x256, 4, 2, 128, SFX##_rs, FA, FB, true)              \
   DG_GEMM_SHAPE(K, 128x256, 2, 2, 128, SFX##_rs, FA, FB, true)              \
   DG_GEMM_SHAPE(K, 128x256w8, 2, 4, 64, SFX##_rs, FA, FB, true)             \
-  DG_GEMM_SHAPE(K, 128x128, 2, 1, 128, SFX##_rs, FA, FB, true)             \
   DG_GEMM_SHAPE(K, 128x128w4, 2, 2, 64, SFX##_rs, FA, FB, true)             \
   DG_GEMM_SHAPE(K, 128x64w2, 2, 1, 64, SFX##_rs, FA, FB, true)
 DG_GEMM_FORMATS(DG_KERNEL(DG_GEMM_KERNEL, FMT_44), , FMT_E4M3, FMT_E4M3)

@@ -8,7 +8,7 @@
 //   DG_DEFINE_FMT_45  E4M3 A x E5M2 B   (suffix _a4b5)
 //   DG_DEFINE_FMT_54  E5M2 A x E4M3 B   (suffix _a5b4)
 //   DG_DEFINE_FMT_55  E5M2 A x E5M2 B   (suffix _a5b5)
-//   DG_DEFINE_MISC    the 1 x 8-wave variant and the quantiser
+//   DG_DEFINE_MISC    the quantiser
 // The kernel headers pass DG_KERNEL(<family>, <group>) as the macro that
 // emits each kernel: <family>_DEF (definition) or <family>_DECL (declaration).
 #pragma once

@@ -120,6 +120,21 @@ def _check_fp8(t, name):
         raise ValueError(f"{name} must be a contiguous device tensor")
 
 
+def operand_fmt(t, fmt, name) -> int:
+    """FP8 format code of operand tensor t.  A float8 dtype names its format;
+    uint8 codes take `fmt` ("e4m3" when None).  An explicit `fmt` that
+    disagrees with a float8 dtype is an error (the bytes would otherwise be
+    decoded in the wrong format)."""
+    torch = _torch()
+    implied = {torch.float8_e4m3fn: DG_FP8_E4M3, torch.float8_e5m2: DG_FP8_E5M2}.get(t.dtype)
+    if fmt is None:
+        return DG_FP8_E4M3 if implied is None else implied
+    code = fmt_code(fmt)
+    if implied is not None and code != implied:
+        raise ValueError(f"{name} is {t.dtype} but its format is given as {fmt!r}")
+    return code
+
+
 def _check_f32(t, name, shape):
     torch = _torch()
     if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
@@ -171,11 +186,11 @@ def _sa_rows(sA, M, K):
                      f"(128 x 128 blocks) or {(M, -(-K // 128))} (1 x 128 blocks)")
 
 
-def gemm_fp8_blockscaled(A, sA, B, sB, out_dtype="bf16", C=None, stream=None, a_fmt="e4m3", b_fmt="e4m3"):
+def gemm_fp8_blockscaled(A, sA, B, sB, out_dtype="bf16", C=None, stream=None, a_fmt=None, b_fmt=None):
     """C[M][N] = block-scaled A[M][K] x B (stored [N][K]) on the device; the
-    operands' FP8 formats are "e4m3" (default) or "e5m2".  sA holds one scale
-    per 128 x 128 block ([ceil(M/128)][K/128]) or per row and 128 columns
-    ([M][K/128])."""
+    operands' FP8 formats are "e4m3" or "e5m2" (None: from a float8 dtype,
+    E4M3 for uint8 codes).  sA holds one scale per 128 x 128 block
+    ([ceil(M/128)][K/128]) or per row and 128 columns ([M][K/128])."""
     _check_fp8(A, "A")
     _check_fp8(B, "B")
     M, K = A.shape
@@ -187,7 +202,7 @@ def gemm_fp8_blockscaled(A, sA, B, sB, out_dtype="bf16", C=None, stream=None, a_
     _check_f32(sB, "sB", (-(-N // 128), -(-K // 128)))
     code = out_code(out_dtype)
     C = _out(C, M, N, code, A)
-    fa, fb = fmt_code(a_fmt), fmt_code(b_fmt)
+    fa, fb = operand_fmt(A, a_fmt, "A"), operand_fmt(B, b_fmt, "B")
     if fa == DG_FP8_E4M3 and fb == DG_FP8_E4M3 and rows == 128:
         st = dg_gemm_fp8_blockscaled(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(),
                                      C.data_ptr(), M, N, K, code, _stream(stream))
@@ -200,7 +215,7 @@ def gemm_fp8_blockscaled(A, sA, B, sB, out_dtype="bf16", C=None, stream=None, a_
 
 
 def grouped_gemm_fp8(A, sA, B, sB, group_offsets, out_dtype="bf16", C=None, stream=None,
-                     a_fmt="e4m3", b_fmt="e4m3"):
+                     a_fmt=None, b_fmt=None):
     """MoE grouped GEMM over contiguous 128-row-padded expert segments."""
     torch = _torch()
     _check_fp8(A, "A")
@@ -217,7 +232,7 @@ def grouped_gemm_fp8(A, sA, B, sB, group_offsets, out_dtype="bf16", C=None, stre
         raise ValueError("group_offsets must be a device int32 tensor of G + 1 entries")
     code = out_code(out_dtype)
     C = _out(C, M_total, N, code, A)
-    fa, fb = fmt_code(a_fmt), fmt_code(b_fmt)
+    fa, fb = operand_fmt(A, a_fmt, "A"), operand_fmt(B, b_fmt, "B")
     if fa == DG_FP8_E4M3 and fb == DG_FP8_E4M3 and rows == 128:
         st = dg_grouped_gemm_fp8(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(),
                                  C.data_ptr(), group_offsets.data_ptr(), G, M_total, N, K, code,
@@ -232,7 +247,7 @@ def grouped_gemm_fp8(A, sA, B, sB, group_offsets, out_dtype="bf16", C=None, stre
 
 
 def grouped_gemm_fp8_segments(A, sA, B, sB, group_offsets, out_dtype="bf16", C=None, stream=None,
-                              a_fmt="e4m3", b_fmt="e4m3"):
+                              a_fmt=None, b_fmt=None):
     """MoE grouped GEMM over packed (unpadded) expert segments with one A
     scale per row, sA [M_total][K/128]; meant for few rows per expert."""
     torch = _torch()
@@ -249,8 +264,8 @@ def grouped_gemm_fp8_segments(A, sA, B, sB, group_offsets, out_dtype="bf16", C=N
         raise ValueError("group_offsets must be a device int32 tensor of G + 1 entries")
     code = out_code(out_dtype)
     C = _out(C, M_total, N, code, A)
-    st = dg_grouped_gemm_fp8_segments(A.data_ptr(), fmt_code(a_fmt), sA.data_ptr(), B.data_ptr(),
-                                      fmt_code(b_fmt), sB.data_ptr(), C.data_ptr(), group_offsets.data_ptr(),
+    st = dg_grouped_gemm_fp8_segments(A.data_ptr(), operand_fmt(A, a_fmt, "A"), sA.data_ptr(), B.data_ptr(),
+                                      operand_fmt(B, b_fmt, "B"), sB.data_ptr(), C.data_ptr(), group_offsets.data_ptr(),
                                       G, M_total, N, K, code, _stream(stream))
     if st != DG_OK:
         raise DGError(st, "dg_grouped_gemm_fp8_segments")

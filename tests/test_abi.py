@@ -178,3 +178,20 @@ def test_binding_refuses_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(dg, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="not built"):
         dg.lib()
+
+
+def test_operand_format_follows_float8_dtype():
+    """The torch helpers take an operand's FP8 format from its float8 dtype
+    and reject an explicit format that contradicts it (CPU tensors: only the
+    dtype is looked at)."""
+    import torch
+    e4, e5, u8 = (torch.zeros(2, dtype=d) for d in (torch.float8_e4m3fn, torch.float8_e5m2, torch.uint8))
+    assert dg.operand_fmt(e5, None, "A") == dg.DG_FP8_E5M2
+    assert dg.operand_fmt(e4, None, "A") == dg.DG_FP8_E4M3
+    assert dg.operand_fmt(u8, None, "A") == dg.DG_FP8_E4M3
+    assert dg.operand_fmt(u8, "e5m2", "A") == dg.DG_FP8_E5M2
+    assert dg.operand_fmt(e5, "e5m2", "B") == dg.DG_FP8_E5M2
+    with pytest.raises(ValueError):
+        dg.operand_fmt(e5, "e4m3", "A")
+    with pytest.raises(ValueError):
+        dg.operand_fmt(e4, dg.DG_FP8_E5M2, "B")

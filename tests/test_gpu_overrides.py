@@ -1,8 +1,8 @@
-"""The tile-choice overrides (DG_FORCE_TILE: 1512 = the 1 x 8-wave variant,
-512 / 256 / 128 = one tile shape for every problem, 2256 = the 256 x 256
-tile for every dense problem; DG_TAIL_TILE: 0 = no
-separate last round, 128 = 128 x 128 tiles for it) give results inside the
-parity bound.  The library reads them once per process, so every setting
+"""The tile-choice overrides (DG_FORCE_TILE: 512 / 256 = one tile shape for
+every problem, 2256 = the 256 x 256 tile for every dense problem, 8256 /
+4128 / 264 = one narrow tile wherever a narrow tile is used; DG_TAIL_TILE:
+0 = no separate last round, 8256 = the 8-wave 128 x 256 tile for it) give
+results inside the parity bound.  The library reads them once per process, so every setting
 runs tests/override_child.py in a child process.  Needs a GPU."""
 import os
 import subprocess
@@ -15,12 +15,11 @@ pytestmark = pytest.mark.gpu
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-@pytest.mark.parametrize("env", [{"DG_FORCE_TILE": "1512"}, {"DG_FORCE_TILE": "512"},
+@pytest.mark.parametrize("env", [{"DG_FORCE_TILE": "512"},
                                  {"DG_FORCE_TILE": "2256"}, {"DG_FORCE_TILE": "8256"},
                                  {"DG_FORCE_TILE": "4128"}, {"DG_FORCE_TILE": "264"},
                                  {"DG_TAIL_TILE": "8256"},
-                                 {"DG_FORCE_TILE": "256"}, {"DG_FORCE_TILE": "128"},
-                                 {"DG_TAIL_TILE": "0"}, {"DG_TAIL_TILE": "128"}],
+                                 {"DG_FORCE_TILE": "256"}, {"DG_TAIL_TILE": "0"}],
                          ids=lambda e: "_".join(f"{k}={v}" for k, v in e.items()))
 def test_tile_override(env):
     full = dict(os.environ)
