@@ -33,9 +33,13 @@ Workloads (seeded, synthetic; see inputs.make_config):
 --op quantize times the activation quantisation that produces A instead
 (4096 x 4096 BF16 in, E4M3 codes and FP32 block scales out; HBM-bound).
 --op torch-matmul times the vendor library's plain BF16 (or FP16) GEMM,
-torch.matmul on 4096^3, as a reference point for the matrix cores' rate;
---dtype fp8 its FP8 GEMM (torch._scaled_mm, one scale per tensor, FP8
-matrix cores).
+torch.matmul on 4096^3, as a reference point for the matrix cores' rate.
+
+Clock settling: before the W warm-up steps the same step is run, untimed,
+for --settle-ms milliseconds (default 500).  The GPU raises its clock over
+the first tens of milliseconds of sustained load, so a short timed region
+that starts right after a few warm-up steps would land partly on that ramp;
+the settle phase makes the timed steps measure the sustained rate.
 """
 from __future__ import annotations
 
@@ -158,9 +162,29 @@ def cpu_baseline_quant(x, block_rows: int, target_s: float = 10.0):
                       "one thread (per-block Python loop)"}
 
 
-def run_timed(step, K: int, W: int, use_graph: bool):
-    """W untimed warm-up steps, then exactly K timed steps between
-    torch.cuda.synchronize() calls.  step(i, stream_handle) enqueues step i.
+def settle(step, settle_ms: float):
+    """Run the step, untimed, for about settle_ms milliseconds of wall time
+    (batches of launches with a synchronisation after each), so that the GPU
+    clock has left its idle level before anything is timed.  Returns the
+    number of steps run."""
+    import torch
+    if settle_ms <= 0:
+        return 0
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(16):
+            step(n, stream.cuda_stream)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def run_timed(step, K: int, W: int, use_graph: bool, settle_ms: float = 0.0):
+    """An untimed settle phase of about settle_ms (see settle()), W untimed
+    warm-up steps, then exactly K timed steps between torch.cuda.synchronize()
+    calls.  step(i, stream_handle) enqueues step i.
 
     With use_graph the K timed steps are captured once into a HIP graph and
     the timed region is one replay of it: kernels of a few microseconds are
@@ -171,6 +195,9 @@ def run_timed(step, K: int, W: int, use_graph: bool):
     import numpy as np
     import torch
     stream = torch.cuda.current_stream()
+    n_settle = settle(step, settle_ms)
+    if n_settle:
+        log(f"settle: {n_settle} untimed steps in ~{settle_ms:.0f} ms before the warm-up")
     for i in range(W):
         step(i, stream.cuda_stream)
     torch.cuda.synchronize()
@@ -227,51 +254,33 @@ def bench_torch_matmul(args):
     """The vendor library's plain GEMM on the same shape, for comparison:
     torch.matmul on BF16 (or FP16) operands, which runs hipBLASLt.  No FP8
     decode, no block scales: a reference point for the matrix cores' rate,
-    not the block-scaled operation.  --dtype fp8: torch._scaled_mm on E4M3
-    operands with one scale per tensor (FP8 matrix cores, BF16 out), the
-    vendor's FP8 rate; its FP8 accumulation is not held to this library's
-    tolerance and it has no block scales."""
+    not the block-scaled operation."""
     import torch
     dev = torch.device("cuda:0")
     M = N = K = 4096
     gen = torch.Generator(device="cpu").manual_seed(2)
     R = args.rotate or 8
-    if args.dtype == "fp8":
-        f8 = torch.float8_e4m3fn
-        one = torch.ones((), dtype=torch.float32, device=dev)
-        ops = [(torch.randn(M, K, generator=gen).to(dev).to(f8),
-                torch.randn(N, K, generator=gen).to(dev).to(f8).t(),          # stored N x K, column-major B
-                torch.empty(M, N, dtype=torch.bfloat16, device=dev)) for _ in range(R)]
+    dt = torch.bfloat16 if args.dtype == "bf16" else torch.float16
+    ops = [(torch.randn(M, K, generator=gen).to(dt).to(dev),
+            torch.randn(K, N, generator=gen).to(dt).to(dev).t().contiguous().t(),   # stored N x K, as B
+            torch.empty(M, N, dtype=dt, device=dev)) for _ in range(R)]
 
-        def step(i, sh):
-            a, b, c = ops[i % R]
-            torch._scaled_mm(a, b, scale_a=one, scale_b=one, out_dtype=torch.bfloat16, out=c)
-    else:
-        dt = torch.bfloat16 if args.dtype == "bf16" else torch.float16
-        ops = [(torch.randn(M, K, generator=gen).to(dt).to(dev),
-                torch.randn(K, N, generator=gen).to(dt).to(dev).t().contiguous().t(),   # stored N x K, as B
-                torch.empty(M, N, dtype=dt, device=dev)) for _ in range(R)]
+    def step(i, sh):                 # torch enqueues on its current stream, which is sh here
+        a, b, c = ops[i % R]
+        torch.matmul(a, b, out=c)
 
-        def step(i, sh):                 # torch enqueues on its current stream, which is sh here
-            a, b, c = ops[i % R]
-            torch.matmul(a, b, out=c)
-
-    ms_step, kern_ms, _ = run_timed(step, args.steps, args.warmup, not args.no_graph)
+    ms_step, kern_ms, _ = run_timed(step, args.steps, args.warmup, not args.no_graph, args.settle_ms)
     flop = 2.0 * M * N * K
     achieved = flop / (kern_ms * 1e-3) / 1e12
-    api = "torch._scaled_mm, one scale per tensor" if args.dtype == "fp8" else "torch.matmul"
-    line = {"metric": f"vendor {args.dtype.upper()} GEMM TFLOPS ({api} / hipBLASLt), same shape, for comparison",
+    line = {"metric": f"vendor {args.dtype.upper()} GEMM TFLOPS (torch.matmul / hipBLASLt), same shape, for comparison",
             "value": round(flop / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.dtype,
             "data": "synthetic",
             "config": {"workload": f"torch_matmul_4096_{args.dtype}", "M": M, "N": N, "K": K,
                        "operand_copies": R, "launch": "eager" if args.no_graph else "hip_graph"},
-            "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
-                         "peak": PEAK_FP8_TFLOPS if args.dtype == "fp8" else PEAK_FP16_TFLOPS,
-                         "unit": "TFLOP/s",
-                         "frac": round(achieved / (PEAK_FP8_TFLOPS if args.dtype == "fp8" else PEAK_FP16_TFLOPS), 4),
-                         "traffic": None},
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": None},
             "cpu_baseline": None, "kernel_ms": round(kern_ms, 5)}
     print(json.dumps(line), flush=True)
 
@@ -308,7 +317,7 @@ def bench_quantize(args):
             raise dg.DGError(st, "bench step")
 
     n = args.steps
-    ms_step, kern_ms, _ = run_timed(step, n, args.warmup, not args.no_graph)
+    ms_step, kern_ms, _ = run_timed(step, n, args.warmup, not args.no_graph, args.settle_ms)
     kern_eager = eager_kernel_ms(step, n, not args.no_graph)
     name = f"quantize_{M}x{K}_bf16_{R_blk}x128"
     achieved = step_bytes / (kern_ms * 1e-3) / 1e9
@@ -340,7 +349,9 @@ def main():
                     help="launch the timed steps one by one from Python instead of replaying a HIP graph")
     ap.add_argument("--op", choices=["gemm", "quantize", "torch-matmul"], default="gemm",
                     help="torch-matmul: the vendor BF16/FP16 GEMM on 4096^3, for comparison")
-    ap.add_argument("--dtype", choices=["bf16", "fp16", "fp8"], default="bf16", help="operand type of --op torch-matmul")
+    ap.add_argument("--dtype", choices=["bf16", "fp16"], default="bf16", help="operand type of --op torch-matmul")
+    ap.add_argument("--settle-ms", type=float, default=500.0,
+                    help="untimed run of the step before the warm-up, so that the GPU clock has settled")
     ap.add_argument("--a-scale", choices=["128x128", "1x128"], default="128x128",
                     help="A scale blocks of the GEMM: 128x128, or one per token and 128 columns")
     ap.add_argument("--fmt", choices=["e4m3", "e5m2"], default="e4m3",
@@ -438,7 +449,7 @@ def main():
             raise dg.DGError(st, "bench step")
 
     K = args.steps
-    ms_step, kern_ms, _ = run_timed(step, K, args.warmup, not args.no_graph)
+    ms_step, kern_ms, _ = run_timed(step, K, args.warmup, not args.no_graph, args.settle_ms)
     kern_eager = eager_kernel_ms(step, K, not args.no_graph)
 
     flop = p.algorithmic_flop()

@@ -1,11 +1,22 @@
 """The numerics behind the choice of the FP16 matrix cores, measured against
 the vendor's FP8 GEMM.  torch._scaled_mm (hipBLASLt, E4M3 operands, unit
 per-tensor scales, FP32 out) accumulates on gfx950's FP8 matrix cores; with
-unit scales it computes exactly the product that the oracle defines for unit
-block scales, so its error against the oracle is the FP8 accumulation's own.
-The test logs the vendor's max err/bound beside this library's and asserts
-only this library's result (the vendor's figure documents the design, it is
-not a requirement).  Needs a GPU; skipped when torch has no FP8 GEMM."""
+unit scales it computes the product that the oracle defines for unit block
+scales, so its error against the oracle is the FP8 accumulation's own.
+
+test_fp8_matrix_cores_drop_small_products is the deterministic evidence:
+operands built so that every group of 8 consecutive K elements of many
+outputs holds one product of 2^16 and seven of 2^2.  An accumulation that
+keeps about 14 bits below the largest product of a group (what the FP8
+matrix-core instruction does) loses small products, up to 28 per group; an
+FP32-grade accumulation keeps them, and the exact result (below 2^24) is
+representable in FP32.  The test asserts that the vendor's FP8 GEMM loses
+them (and is exact on the outputs whose products span only 2^2 .. 2^9) and
+that this library returns the exact value everywhere.
+
+The Gaussian cases log the vendor's max err/bound beside this library's and
+assert only this library's result.  Needs a GPU; skipped when torch has no
+FP8 GEMM."""
 import sys
 
 import numpy as np
@@ -20,31 +31,88 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def ratio(C, Cr, mass):
-    Cg = C.float().cpu().numpy().astype(np.float64)
-    return float((np.abs(Cg - Cr) / oracle.tolerance(Cr, mass, "f32")).max())
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def vendor_fp8(A8, B8):
+    """torch._scaled_mm on E4M3 tensors A [M][K], B [N][K] (B column-major),
+    unit scales, FP32 out; skips the test where the torch build has none."""
+    if not hasattr(torch, "_scaled_mm"):
+        pytest.skip("torch has no FP8 GEMM")
+    one = torch.ones((), device=DEV)
+    try:
+        C = torch._scaled_mm(A8.to(DEV), B8.to(DEV).t(), scale_a=one, scale_b=one, out_dtype=torch.float32)
+    except RuntimeError as e:      # pragma: no cover - depends on the torch build
+        pytest.skip(f"torch._scaled_mm unavailable here: {e}")
+    torch.cuda.synchronize()
+    return C.cpu().numpy().astype(np.float64)
+
+
+def ours(qa, qb):
+    M, K = qa.shape
+    N = qb.shape[0]
+    sA = np.ones((-(-M // 128), -(-K // 128)), np.float32)
+    sB = np.ones((-(-N // 128), -(-K // 128)), np.float32)
+    C = dg.gemm_fp8_blockscaled(t(qa), t(sA), t(qb), t(sB), "f32")
+    torch.cuda.synchronize()
+    return C.cpu().numpy().astype(np.float64), sA, sB
+
+
+def test_fp8_matrix_cores_drop_small_products():
+    M = N = 64
+    K = 256
+    # Row i of A and row j of B hold 256 at one position of every group of 8
+    # (a different position per row, the same for A row i and B row i) and 2
+    # elsewhere, so output (i, j) sums, per group, one 2^16 (both 256) and
+    # seven 2^2 when i and j share the position, else products of 2^9 and 2^2.
+    pos = (np.arange(M) * 5) % 8
+    k = np.arange(K)
+    big_a = (k[None, :] % 8) == pos[:, None]
+    a = np.where(big_a, 256.0, 2.0).astype(np.float32)
+    b = a[:N].copy()
+    A8 = torch.from_numpy(a).to(torch.float8_e4m3fn)
+    B8 = torch.from_numpy(b).to(torch.float8_e4m3fn)
+    qa, qb = A8.view(torch.uint8).numpy(), B8.view(torch.uint8).numpy()
+    exact = a.astype(np.float64) @ b.astype(np.float64).T          # integers below 2^24: exact
+    same = pos[:, None] == pos[None, :N]
+    groups = K // 8
+    assert np.all(exact[same] == groups * (65536 + 7 * 4))
+    assert exact.max() < 2 ** 24
+
+    Cd, sA, sB = ours(qa, qb)
+    Cr, _ = oracle.gemm_blockscaled(qa, sA, qb, sB)
+    assert np.array_equal(Cr, exact)
+    assert np.array_equal(Cd, exact), "this library must be exact here"
+
+    Cv = vendor_fp8(A8, B8)
+    lost = exact[same] - Cv[same]
+    log(f"  crafted groups: exact {exact[same][0]:.0f}, vendor FP8 GEMM {Cv[same][0]:.0f} "
+        f"(lost {lost.min():.0f} .. {lost.max():.0f} of {groups * 28} in small products), this library "
+        f"{Cd[same][0]:.0f}")
+    # every output whose groups pair 2^16 with 2^2 loses small products (all
+    # of them when each product is cut to the window, part of them when the
+    # small ones are summed first), never more, and the rest is exact
+    assert np.all(lost > 0), "the vendor FP8 GEMM kept every product below its window"
+    assert np.all(lost <= groups * 28) and np.all(lost % 4 == 0)
+    assert np.array_equal(Cv[~same], exact[~same])
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (64, 144, 128), (1024, 1024, 1024)])
 def test_fp8_matrix_core_accumulation_vs_this_library(M, N, K):
-    if not hasattr(torch, "_scaled_mm"):
-        pytest.skip("torch has no FP8 GEMM")
     rng = np.random.default_rng(M + K)
     A = torch.from_numpy(rng.standard_normal((M, K), dtype=np.float32)).to(torch.float8_e4m3fn)
     B = torch.from_numpy(rng.standard_normal((N, K), dtype=np.float32)).to(torch.float8_e4m3fn)
     qa, qb = A.view(torch.uint8).numpy(), B.view(torch.uint8).numpy()
-    sA = np.ones((-(-M // 128), K // 128), np.float32)
-    sB = np.ones((-(-N // 128), K // 128), np.float32)
-    one = torch.ones((), device=DEV)
-    try:
-        Cv = torch._scaled_mm(A.to(DEV), B.to(DEV).t(), scale_a=one, scale_b=one, out_dtype=torch.float32)
-    except RuntimeError as e:      # pragma: no cover - depends on the torch build
-        pytest.skip(f"torch._scaled_mm unavailable here: {e}")
-    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
-    Cd = dg.gemm_fp8_blockscaled(t(qa), t(sA), t(qb), t(sB), "f32")
-    torch.cuda.synchronize()
+    Cv = vendor_fp8(A, B)
+    Cd, sA, sB = ours(qa, qb)
     Cr, mass = oracle.gemm_blockscaled(qa, sA, qb, sB)
-    rv, rd = ratio(Cv, Cr, mass), ratio(Cd, Cr, mass)
-    print(f"  {M}x{N}x{K} FP32 out: vendor FP8 GEMM max err/bound = {rv:.3g}, this library = {rd:.3g}",
-          file=sys.stderr, flush=True)
+    bound = oracle.tolerance(Cr, mass, "f32")
+    rv = float((np.abs(Cv - Cr) / bound).max())
+    rd = float((np.abs(Cd - Cr) / bound).max())
+    log(f"  {M}x{N}x{K} FP32 out: vendor FP8 GEMM max err/bound = {rv:.3g}, this library = {rd:.3g}")
     assert rd <= 1.0
