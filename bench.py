@@ -35,11 +35,13 @@ Workloads (seeded, synthetic; see inputs.make_config):
 --op torch-matmul times the vendor library's plain BF16 (or FP16) GEMM,
 torch.matmul on 4096^3, as a reference point for the matrix cores' rate.
 
-Clock settling: before the W warm-up steps the same step is run, untimed,
-for --settle-ms milliseconds (default 500).  The GPU raises its clock over
-the first tens of milliseconds of sustained load, so a short timed region
-that starts right after a few warm-up steps would land partly on that ramp;
-the settle phase makes the timed steps measure the sustained rate.
+Clock settling: right before the timed region the same work is run,
+untimed, for --settle-ms milliseconds (default 300; graph mode replays the
+captured graph).  Under load the GPU's clock takes some 20-30 ms to reach
+its sustained level (on 4096^3 the first ~200 launches from idle run up to
+35 % slower than later ones), and capturing the graph leaves the GPU idle
+for a while; without the settle phase a short timed region (20 steps of
+0.1 ms) lands on that ramp.  --settle-ms 0 gives the cold figure.
 """
 from __future__ import annotations
 
@@ -162,42 +164,39 @@ def cpu_baseline_quant(x, block_rows: int, target_s: float = 10.0):
                       "one thread (per-block Python loop)"}
 
 
-def settle(step, settle_ms: float):
-    """Run the step, untimed, for about settle_ms milliseconds of wall time
-    (batches of launches with a synchronisation after each), so that the GPU
-    clock has left its idle level before anything is timed.  Returns the
-    number of steps run."""
+def settle(launch, settle_ms: float, per_batch: int = 1):
+    """Enqueue launch() back to back, untimed, for about settle_ms
+    milliseconds of wall time (a synchronisation after every per_batch
+    launches), so that the GPU clock has reached its level under sustained
+    load.  Returns the number of launches."""
     import torch
     if settle_ms <= 0:
         return 0
-    stream = torch.cuda.current_stream()
     t0 = time.perf_counter()
     n = 0
     while (time.perf_counter() - t0) * 1e3 < settle_ms:
-        for _ in range(16):
-            step(n, stream.cuda_stream)
+        for _ in range(per_batch):
+            launch(n)
             n += 1
         torch.cuda.synchronize()
     return n
 
 
 def run_timed(step, K: int, W: int, use_graph: bool, settle_ms: float = 0.0):
-    """An untimed settle phase of about settle_ms (see settle()), W untimed
-    warm-up steps, then exactly K timed steps between torch.cuda.synchronize()
-    calls.  step(i, stream_handle) enqueues step i.
+    """W untimed warm-up steps, an untimed settle phase of about settle_ms
+    right before the timed region (see settle()), then exactly K timed steps
+    between torch.cuda.synchronize() calls.  step(i, stream_handle) enqueues
+    step i.
 
     With use_graph the K timed steps are captured once into a HIP graph and
     the timed region is one replay of it: kernels of a few microseconds are
-    otherwise paced by the host's launch rate rather than by the GPU (the
-    graph is replayed once, untimed, before the timed replay).  Returns
+    otherwise paced by the host's launch rate rather than by the GPU.  The
+    settle phase then replays the same graph (at least once).  Returns
     (wall ms per step, kernel ms per step from HIP events on the launch
     stream, per-step event times or None)."""
     import numpy as np
     import torch
     stream = torch.cuda.current_stream()
-    n_settle = settle(step, settle_ms)
-    if n_settle:
-        log(f"settle: {n_settle} untimed steps in ~{settle_ms:.0f} ms before the warm-up")
     for i in range(W):
         step(i, stream.cuda_stream)
     torch.cuda.synchronize()
@@ -208,8 +207,11 @@ def run_timed(step, K: int, W: int, use_graph: bool, settle_ms: float = 0.0):
             for i in range(K):
                 step(W + i, h)
         torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
+        n = settle(lambda _: g.replay(), settle_ms) if settle_ms > 0 else 0
+        if n == 0:
+            g.replay()
+            torch.cuda.synchronize()
+        log(f"settle: {max(n, 1)} untimed replays of the {K}-step graph right before the timed one")
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         t_start = time.perf_counter()
         ev[0].record(stream)
@@ -220,6 +222,9 @@ def run_timed(step, K: int, W: int, use_graph: bool, settle_ms: float = 0.0):
         per = None
         kern_ms = float(ev[0].elapsed_time(ev[1])) / K
     else:
+        n = settle(lambda i: step(W + K + i, stream.cuda_stream), settle_ms, per_batch=16)
+        if n:
+            log(f"settle: {n} untimed steps right before the timed ones")
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
         t_start = time.perf_counter()
         for i in range(K):
@@ -350,8 +355,9 @@ def main():
     ap.add_argument("--op", choices=["gemm", "quantize", "torch-matmul"], default="gemm",
                     help="torch-matmul: the vendor BF16/FP16 GEMM on 4096^3, for comparison")
     ap.add_argument("--dtype", choices=["bf16", "fp16"], default="bf16", help="operand type of --op torch-matmul")
-    ap.add_argument("--settle-ms", type=float, default=500.0,
-                    help="untimed run of the step before the warm-up, so that the GPU clock has settled")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed run of the step right before the timed region, so that the GPU clock has "
+                         "reached its sustained level (0: none)")
     ap.add_argument("--a-scale", choices=["128x128", "1x128"], default="128x128",
                     help="A scale blocks of the GEMM: 128x128, or one per token and 128 columns")
     ap.add_argument("--fmt", choices=["e4m3", "e5m2"], default="e4m3",

@@ -3,3 +3,4 @@
 #define DG_DEFINE_FMT_45
 #include "gemm_f16mma.hpp"
 #include "gemm_skinny.hpp"
+#include "gemm_sharedb.hpp"

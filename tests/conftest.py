@@ -4,8 +4,10 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-if ROOT not in sys.path:
-    sys.path.insert(0, ROOT)
+HERE = os.path.dirname(os.path.abspath(__file__))
+for _p in (ROOT, HERE):
+    if _p not in sys.path:
+        sys.path.insert(0, _p)
 
 
 def pytest_configure(config):
@@ -14,6 +16,21 @@ def pytest_configure(config):
 
 
 GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Max err/bound per parity case: the full-size workloads and the ten
+    cases closest to the bound."""
+    import parity_log
+    rows = parity_log.RATIOS
+    if not rows:
+        return
+    tr = terminalreporter
+    full = [r for r in rows if r[0].startswith("workload")]
+    worst = sorted(rows, key=lambda r: -r[1])[:10]
+    tr.write_line(f"parity: {len(rows)} comparisons, max err/bound {max(r[1] for r in rows):.3g}")
+    for name, ratio in full + [r for r in worst if r not in full]:
+        tr.write_line(f"  {ratio:8.3g}  {name}")
 
 
 @pytest.fixture(scope="session")

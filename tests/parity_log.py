@@ -1,0 +1,10 @@
+"""Max err/bound of every parity comparison in this test session.
+
+Tests call record(); tests/conftest.py prints the table at the end of the
+session (also under -q, where pytest hides what passing tests print), so
+that a run's log shows how close each case came to the bound."""
+RATIOS: list[tuple[str, float]] = []
+
+
+def record(name: str, ratio: float) -> None:
+    RATIOS.append((name, float(ratio)))

@@ -15,6 +15,8 @@ import numpy as np
 import pytest
 import torch
 
+import parity_log
+
 import oracle
 from moe_grouped_gemm_block_amd import dg
 from moe_grouped_gemm_block_amd import inputs as I
@@ -69,6 +71,7 @@ def check(p: I.Problem, Cg: np.ndarray, rows=None, cols=None, what=""):
     err = np.abs(Cg - Cr)
     ratio = float((err / bound).max()) if err.size else 0.0
     log(f"  {what or p.name}: max err/bound = {ratio:.3g}")
+    parity_log.record(what or p.name, ratio)
     assert np.all(np.isfinite(Cg))
     bad = np.argwhere(err > bound)
     assert len(bad) == 0, f"{len(bad)} elements out of tolerance, first {bad[:5].tolist()}"
@@ -243,6 +246,7 @@ def test_workload_full(i, out):
     acc = float((err / (1e-5 * mass + 1e-6)).max())
     log(f"  workload {i} {out}: max err/bound = {ratio:.3g} (err / (1e-5 mass + 1e-6) = {acc:.3g}), "
         f"{Cg.size} outputs")
+    parity_log.record(f"workload {i} {out} ({Cg.size} outputs)", ratio)
     assert np.all(np.isfinite(Cg))
     bad = np.argwhere(err > bound)
     assert len(bad) == 0, f"{len(bad)} elements out of tolerance, first {bad[:5].tolist()}"

@@ -9,6 +9,8 @@ import numpy as np
 import pytest
 import torch
 
+import parity_log
+
 import oracle
 from moe_grouped_gemm_block_amd import dg
 from moe_grouped_gemm_block_amd import inputs as I
@@ -55,6 +57,7 @@ def test_random_dense(M, N, K, out):
     bound = oracle.tolerance(Cr, mass, out)
     ratio = float((np.abs(Cg - Cr) / bound).max())
     log(f"  random {M}x{N}x{K} {out}: max err/bound = {ratio:.3g}")
+    parity_log.record(f"random {M}x{N}x{K} {out}", ratio)
     assert np.all(np.isfinite(Cg)) and ratio <= 1.0
 
 
@@ -93,6 +96,7 @@ def test_random_grouped(counts, N, K, out):
     Cr, mass = oracle.grouped_gemm(qA, sA, qB, sB, offs)
     ratio = float((np.abs(Cg - Cr) / oracle.tolerance(Cr, mass, out)).max()) if Cg.size else 0.0
     log(f"  random grouped G={G} rows={int(offs[-1])} N={N} K={K} {out}: max err/bound = {ratio:.3g}")
+    parity_log.record(f"random grouped G={G} N={N} K={K} {out}", ratio)
     assert np.all(np.isfinite(Cg)) and ratio <= 1.0
     for e, c in enumerate(counts):
         assert np.all(Cg[offs[e] + c:offs[e + 1]] == 0)

@@ -9,6 +9,8 @@ import numpy as np
 import pytest
 import torch
 
+import parity_log
+
 import oracle
 from moe_grouped_gemm_block_amd import dg
 from moe_grouped_gemm_block_amd import inputs as I
@@ -36,6 +38,7 @@ def check(Cg, Cr, mass, out_dtype, what):
     bound = oracle.tolerance(Cr, mass, out_dtype)
     err = np.abs(Cg - Cr)
     log(f"  {what}: max err/bound = {float((err / bound).max()) if err.size else 0:.3g}")
+    parity_log.record(f"tails {what}", float((err / bound).max()) if err.size else 0.0)
     assert np.all(np.isfinite(Cg))
     bad = np.argwhere(err > bound)
     assert len(bad) == 0, f"{len(bad)} elements out of tolerance, first {bad[:5].tolist()}"

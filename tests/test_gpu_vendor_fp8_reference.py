@@ -23,6 +23,8 @@ import numpy as np
 import pytest
 import torch
 
+import parity_log
+
 import oracle
 from moe_grouped_gemm_block_amd import dg
 
@@ -115,4 +117,5 @@ def test_fp8_matrix_core_accumulation_vs_this_library(M, N, K):
     rv = float((np.abs(Cv - Cr) / bound).max())
     rd = float((np.abs(Cd - Cr) / bound).max())
     log(f"  {M}x{N}x{K} FP32 out: vendor FP8 GEMM max err/bound = {rv:.3g}, this library = {rd:.3g}")
+    parity_log.record(f"vendor-comparison {M}x{N}x{K} f32 (vendor FP8 GEMM: {rv:.3g})", rd)
     assert rd <= 1.0
