@@ -7,6 +7,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "dg.h"
@@ -429,14 +430,16 @@ int dg_quantize_fp8_blockscaled(const void* X, int in_dtype, void* Q, float* S, 
   if (K % dg::KBLK != 0 || K > kMaxK) return DG_ERR_UNSUPPORTED;
   dg::QuantArgs a{X, static_cast<uint8_t*>(Q), S, int(M), int(K)};
   const int64_t Kb = K / dg::KBLK;
-  const int64_t blocks = block_rows == 128 ? ((M + 127) / 128) * Kb : (M * Kb + 15) / 16;
+  // one workgroup per 128 x 128 block, or per 32 1 x 128 blocks
+  const int64_t blocks = block_rows == 128 ? ((M + 127) / 128) * Kb : (M * Kb + 31) / 32;
   if (blocks > INT32_MAX) return DG_ERR_UNSUPPORTED;
   const bool bf16 = in_dtype == DG_IN_BF16;
   const void* fn = block_rows == 128
       ? (bf16 ? reinterpret_cast<const void*>(dg::dg_quant_128x128_bf16) : reinterpret_cast<const void*>(dg::dg_quant_128x128_f32))
       : (bf16 ? reinterpret_cast<const void*>(dg::dg_quant_1x128_bf16) : reinterpret_cast<const void*>(dg::dg_quant_1x128_f32));
   void* kargs[] = {&a};
-  hipError_t err = hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(256), kargs, 0, stream);
+  hipError_t err = hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(block_rows == 128 ? 1024 : 256), kargs, 0,
+                                   stream);
   return err == hipSuccess ? DG_OK : DG_ERR_LAUNCH;
 }
 

@@ -132,9 +132,13 @@ __device__ __forceinline__ void gemm_sharedb_body(const GemmArgs& p) {
   // K position is added per load)
   const uint32_t a_lane = uint32_t(r16 * K);
   // B: the tile's rows (columns of C); rows past N read 0.  Wave w loads
-  // tile rows 32 w + 8 c + lane / 8, 16 bytes at 16 (lane % 8), c = 0..3.
+  // tile rows 32 w + 8 c + lr, 16 bytes at 16 lg, c = 0..3, where (lr, lg)
+  // is a permutation of the lane's bits: lr = lane bits {0, 1, 4}, lg =
+  // lane bits {5, 2, 3}.  Each load instruction still covers 8 whole rows;
+  // the permutation is what makes the FP16 stores into LDS conflict-free
+  // (see convert_b).
   const __amdgpu_buffer_rsrc_t rB = buffer_rsrc(p.B + (size_t)n0 * K, max(0, min(N - n0, BN)) * K);
-  const int lr = lane >> 3, lg = lane & 7;
+  const int lr = (lane & 3) | ((lane >> 2) & 4), lg = ((lane >> 5) & 1) | ((lane >> 1) & 6);
   const uint32_t b_lane = uint32_t((wave * 32 + lr) * K);      // + K position per load
 
   u32x4 araw[MI][2], braw[4];
@@ -166,6 +170,12 @@ __device__ __forceinline__ void gemm_sharedb_body(const GemmArgs& p) {
   // brow_of_col(32 w + 8 c + lr) = row0 + 4 c, whose swizzle is
   // swzb(4 c + lr % 4) = (lr % 4) | (p(c) << 2): the byte offset inside the
   // stage is row0 * 256 + 1024 c + 16 ((2 lg + h) ^ (lr % 4)), XOR 64 p(c).
+  // A ds_write_b128 was measured to conflict when 8 consecutive lanes hit
+  // fewer than 8 distinct 16-byte positions of a 128-byte window (lanes
+  // 8k .. 8k+7 of one row wrote granules of one parity: 2-way, 8 extra
+  // cycles per store); with the lane bits permuted as above, every group of
+  // 8 consecutive lanes covers two rows whose swizzles differ in bit 0, and
+  // the 16-lane and read-clock groupings stay conflict-free too.
   const int row0 = brow_of_col(wave * 32 + lr);
   const uint32_t wr_off[2] = {uint32_t(row0 * ROWB + 16 * ((2 * lg) ^ (lr & 3))),
                               uint32_t(row0 * ROWB + 16 * ((2 * lg + 1) ^ (lr & 3)))};

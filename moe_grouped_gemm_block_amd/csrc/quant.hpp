@@ -17,8 +17,8 @@
 // to s_n = s 2^-e in [0.5, 1) by its binary exponent e (exact, subnormal s
 // included) and each |x| to a = |x| 2^-e (exact: a <= |x| / s * s_n < 448 can
 // not overflow, and an a that underflows is far below the first E4M3
-// midpoint).  An approximate quotient y = a * fp32(1 / s_n), within a few
-// ulp of a / s_n, only picks the two E4M3 grid values lo < hi around it (lo
+// midpoint).  An approximate quotient y = a * inv_n (inv_n = 1 / s_n within
+// one ulp), within a few ulp of a / s_n, only picks the two E4M3 grid values lo < hi around it (lo
 // read off y's bits); the nearest grid value of the exact quotient is always
 // one of them, because grid steps are at least 2^-4 of the value.  The
 // choice is then exact: the midpoint m = (lo + hi) / 2 has at most 5
@@ -28,7 +28,8 @@
 // rounding through 53 bits is innocuous for one division of 24-bit numbers).
 //
 // Memory-bound: each element is read once (2 or 4 bytes) and written once
-// (1 byte); about 20 FP32 / integer instructions per element.
+// (1 byte).  The encoder above takes about 20 instructions per element; the
+// kernels use it only as the fallback of a cheaper one (fast_codes4 below).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -49,14 +50,16 @@ struct QuantArgs {
 struct ScaleNorm {
   int e;        // s = s_n 2^e
   float s_n;    // in [0.5, 1)
-  float inv_n;  // fp32(1 / s_n), in (1, 2]
+  float inv_n;  // 1 / s_n within one ulp, in (1, 2]
 };
 
 __device__ __forceinline__ ScaleNorm scale_norm(float s) {
   ScaleNorm n;
   n.e = __builtin_amdgcn_frexp_expf(s);
   n.s_n = __builtin_amdgcn_frexp_mantf(s);
-  n.inv_n = 1.0f / n.s_n;
+  // only an approximation is needed (the decisions below are exact): the
+  // hardware reciprocal, within one ulp
+  n.inv_n = __builtin_amdgcn_rcpf(n.s_n);
   return n;
 }
 
@@ -99,131 +102,211 @@ __device__ __forceinline__ float scale_of(float amax) {
 // BF16 bits -> float (exact)
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// 128 x 128 blocks: one workgroup of 256 threads per block, block index
-// rb * Kb + kb; thread t holds row t/2, columns 64 (t%2) .. 64 (t%2) + 63.
-template <bool IN_BF16>
-__device__ __forceinline__ void quant128_body(const QuantArgs& p) {
-  const int Kb = p.K / 128;
-  const int rb = blockIdx.x / Kb, kb = blockIdx.x % Kb;
-  const int t = threadIdx.x, r = t >> 1, h = t & 1;
-  const int m = rb * 128 + r;
-  const bool valid = m < p.M;
-  const size_t e0 = size_t(m) * p.K + size_t(kb) * 128 + 64 * h;   // first element of this thread
-  float v[64];
-  if (valid) {
-    if constexpr (IN_BF16) {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.X) + e0);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint4 w = src[i];
-        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[8 * i + 2 * j] = bf16_to_f32(u[j] & 0xFFFFu);
-          v[8 * i + 2 * j + 1] = bf16_to_f32(u[j] >> 16);
-        }
-      }
-    } else {
-      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(p.X) + e0);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float4 w = src[i];
-        v[4 * i] = w.x; v[4 * i + 1] = w.y; v[4 * i + 2] = w.z; v[4 * i + 3] = w.w;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) v[i] = 0.f;
-  }
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 64; ++i) amax = fmaxf(amax, __builtin_fabsf(v[i]));
-  amax = wave_max(amax);
-  __shared__ float wmax[4];
-  if ((t & 63) == 0) wmax[t >> 6] = amax;
-  __syncthreads();
-  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  const float s = scale_of(amax);
-  const ScaleNorm sn = scale_norm(s);
-  if (valid) {
-    uint4* dst = reinterpret_cast<uint4*>(p.Q + e0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t w[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t packed = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) packed |= e4m3_code(v[16 * i + 4 * j + b], sn) << (8 * b);
-        w[j] = packed;
-      }
-      dst[i] = uint4{w[0], w[1], w[2], w[3]};
-    }
-  }
-  if (t == 0) p.S[size_t(rb) * Kb + kb] = s;
+// ---- fast encoder -----------------------------------------------------------
+// Per block, r = fp32(1 / s_n) 2^-e, so x r is x / s up to three FP32
+// roundings.  With r_lo = fp32(r (1 - 2^-20)) and r_hi = fp32(r (1 + 2^-20)),
+// y_lo = fp32(x r_lo) and y_hi = fp32(x r_hi) bracket the exact quotient x / s
+// (each rounding moves a value by at most 2^-24 of it).  The hardware
+// conversion (v_cvt_scalef32_pk_fp8_f32, scale 1: round to nearest even in
+// OCP E4M3) is monotone, so when it gives the same code for y_lo and y_hi that
+// is also the code of x / s.  The codes differ only when a midpoint of the E4M3
+// grid lies within about 2^-20 of x / s (or at the top of the range, where
+// y_hi may exceed 448 and convert to NaN): those lanes, and every element of a
+// block whose r is not a normal FP32 number (scales near the ends of the FP32
+// range), are encoded by the exact encoder e4m3_code instead.  Zero, -0,
+// subnormal E4M3 codes and saturation need no separate treatment.
+struct FastScale {
+  float r_lo, r_hi;
+  bool ok;      // r is a normal FP32 number
+};
+
+__device__ __forceinline__ FastScale fast_scale(const ScaleNorm& n) {
+  const float r = __builtin_ldexpf(n.inv_n, -n.e);
+  FastScale f;
+  f.r_lo = r * (1.0f - 0x1p-20f);
+  f.r_hi = r * (1.0f + 0x1p-20f);
+  f.ok = __builtin_fabsf(r) >= 0x1p-125f && __builtin_fabsf(r) <= 0x1p+126f;
+  return f;
 }
 
-// 1 x 128 blocks.  Block b = row * Kb + kb covers elements [128 b, 128 b + 128)
-// of the row-major matrix, so consecutive blocks are contiguous: a wave
-// takes 4 of them (16 lanes each, 8 elements per lane: one 16-byte load of
-// BF16, two of FP32), a workgroup 16.  amax is reduced within the 16 lanes.
-__device__ __forceinline__ float group16_max(float v) {
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+typedef short v2i16 __attribute__((ext_vector_type(2)));
+
+// Codes of y0..y3 (value i in byte i) by the hardware conversion.
+__device__ __forceinline__ uint32_t hw_codes4(float y0, float y1, float y2, float y3) {
+  v2i16 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2i16{0, 0}, y0, y1, 1.0f, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, y2, y3, 1.0f, true);
+  return __builtin_bit_cast(uint32_t, w);
+}
+
+// Four values -> four E4M3 codes (value i in byte i); `miss` is raised when
+// the bracket does not decide one of them.
+__device__ __forceinline__ uint32_t fast_codes4(float x0, float x1, float x2, float x3, const FastScale& f,
+                                                bool& miss) {
+  const uint32_t lo = hw_codes4(x0 * f.r_lo, x1 * f.r_lo, x2 * f.r_lo, x3 * f.r_lo);
+  const uint32_t hi = hw_codes4(x0 * f.r_hi, x1 * f.r_hi, x2 * f.r_hi, x3 * f.r_hi);
+  miss = miss | (lo != hi);
+  return lo;
+}
+
+__device__ __forceinline__ uint32_t exact_codes4(float x0, float x1, float x2, float x3, const ScaleNorm& sn) {
+  return e4m3_code(x0, sn) | (e4m3_code(x1, sn) << 8) | (e4m3_code(x2, sn) << 16) | (e4m3_code(x3, sn) << 24);
+}
+
+// ---- 1 x 128 blocks ----------------------------------------------------------
+// Block b = row * Kb + kb covers elements [128 b, 128 b + 128) of the
+// row-major matrix, so consecutive blocks are contiguous.  An 8-lane group
+// takes one block (16 elements per lane: two 16-byte loads of BF16, four of
+// FP32), a wave 8 consecutive blocks, a workgroup 32.  amax is reduced within
+// the 8 lanes by DPP lane permutations.
+__device__ __forceinline__ float group8_max(float v) {
+  // lane i of each 8-lane group takes the max with lane 7 - i (half-row
+  // mirror), then with lane 3 - i of its quad, then with lane i ^ 1: after
+  // the three steps every lane holds the max of its 8 lanes
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                     0x141, 0xF, 0xF, false)));   // row_half_mirror
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                     0x1B, 0xF, 0xF, false)));    // quad_perm 3,2,1,0
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                     0xB1, 0xF, 0xF, false)));    // quad_perm 1,0,3,2
   return v;
+}
+
+template <bool IN_BF16>
+struct Q1Buf {
+  uint4 w[IN_BF16 ? 2 : 4];
+};
+
+template <bool IN_BF16>
+__device__ __forceinline__ float q1_value(const Q1Buf<IN_BF16>& b, int i) {
+  if constexpr (IN_BF16) {
+    const uint4 w = b.w[i / 8];
+    const uint32_t u = (i % 8) < 2 ? w.x : (i % 8) < 4 ? w.y : (i % 8) < 6 ? w.z : w.w;
+    return (i & 1) ? __uint_as_float(u & 0xFFFF0000u) : bf16_to_f32(u & 0xFFFFu);
+  } else {
+    const uint4 w = b.w[i / 4];
+    return __uint_as_float((i % 4) == 0 ? w.x : (i % 4) == 1 ? w.y : (i % 4) == 2 ? w.z : w.w);
+  }
+}
+
+template <bool IN_BF16>
+__device__ __forceinline__ void q1_load(Q1Buf<IN_BF16>& b, const QuantArgs& p, long long blk, long long nblk) {
+  const int lane = threadIdx.x & 63;
+  constexpr int N = IN_BF16 ? 2 : 4;
+  if (blk < nblk) {
+    const size_t e0 = size_t(blk) * 128 + size_t(lane & 7) * 16;
+    const uint4* src = IN_BF16 ? reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.X) + e0)
+                               : reinterpret_cast<const uint4*>(static_cast<const float*>(p.X) + e0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) b.w[i] = src[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) b.w[i] = uint4{0u, 0u, 0u, 0u};   // joins the reduction
+  }
+}
+
+template <bool IN_BF16>
+__device__ __forceinline__ void q1_process(const Q1Buf<IN_BF16>& b, const QuantArgs& p, long long blk,
+                                           long long nblk) {
+  const int lane = threadIdx.x & 63;
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, __builtin_fabsf(q1_value(b, i)));
+  amax = group8_max(amax);
+  const float s = scale_of(amax);
+  const ScaleNorm sn = scale_norm(s);
+  const FastScale fs = fast_scale(sn);
+  if (blk < nblk) {
+    bool flag = !fs.ok;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = fast_codes4(q1_value(b, 4 * j), q1_value(b, 4 * j + 1), q1_value(b, 4 * j + 2),
+                         q1_value(b, 4 * j + 3), fs, flag);
+    if (flag) {                                   // rare: redo this lane's codes exactly
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = exact_codes4(q1_value(b, 4 * j), q1_value(b, 4 * j + 1), q1_value(b, 4 * j + 2),
+                            q1_value(b, 4 * j + 3), sn);
+    }
+    *reinterpret_cast<uint4*>(p.Q + size_t(blk) * 128 + size_t(lane & 7) * 16) = uint4{w[0], w[1], w[2], w[3]};
+    if ((lane & 7) == 0) p.S[blk] = s;
+  }
 }
 
 template <bool IN_BF16>
 __device__ __forceinline__ void quant1_body(const QuantArgs& p) {
   const long long nblk = (long long)p.M * (p.K / 128);
-  const int lane = threadIdx.x & 63;
-  const long long b = (long long)blockIdx.x * 16 + (threadIdx.x >> 6) * 4 + (lane >> 4);
-  const bool valid = b < nblk;
-  const size_t e0 = size_t(b) * 128 + size_t(lane & 15) * 8;   // first element of this lane
-  float v[8];
-  if (valid) {
-    if constexpr (IN_BF16) {
-      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.X) + e0);
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+  const long long blk = (long long)blockIdx.x * 32 + (threadIdx.x >> 3);   // 32 blocks per workgroup
+  Q1Buf<IN_BF16> b;
+  q1_load(b, p, blk, nblk);
+  q1_process(b, p, blk, nblk);
+}
+
+// ---- 128 x 128 blocks --------------------------------------------------------
+// One workgroup of 1024 threads per block (block index rb * Kb + kb); thread
+// t holds row t / 8, columns 16 (t % 8) .. 16 (t % 8) + 15 of the block, so a
+// wave reads 8 whole rows (whole 128-byte lines) and writes 8 whole rows of
+// codes.  The block amax goes through a wave reduction and 16 per-wave
+// maxima in LDS.  (Four threads per row with 32 values each, or a persistent
+// workgroup that loaded the next block while encoding the current one, were
+// slower: fewer waves in flight.)
+template <bool IN_BF16>
+__device__ __forceinline__ void quant128_body(const QuantArgs& p) {
+  __shared__ float wmax[16];
+  const int Kb = p.K / 128;
+  const int rb = blockIdx.x / Kb, kb = blockIdx.x - rb * Kb;
+  const int t = threadIdx.x;
+  const int m = rb * 128 + (t >> 3);
+  const size_t e0 = size_t(m) * p.K + size_t(kb) * 128 + 16 * (t & 7);
+  // the same 16-value layout as the 1 x 128 kernel (Q1Buf); rows past M read 0
+  Q1Buf<IN_BF16> b;
+  constexpr int N = IN_BF16 ? 2 : 4;
+  if (m < p.M) {
+    const uint4* src = IN_BF16 ? reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.X) + e0)
+                               : reinterpret_cast<const uint4*>(static_cast<const float*>(p.X) + e0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[2 * j] = bf16_to_f32(u[j] & 0xFFFFu);
-        v[2 * j + 1] = bf16_to_f32(u[j] >> 16);
-      }
-    } else {
-      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(p.X) + e0);
-      const float4 w0 = src[0], w1 = src[1];
-      v[0] = w0.x; v[1] = w0.y; v[2] = w0.z; v[3] = w0.w;
-      v[4] = w1.x; v[5] = w1.y; v[6] = w1.z; v[7] = w1.w;
-    }
+    for (int i = 0; i < N; ++i) b.w[i] = src[i];
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.f;                    // joins the reduction, stores nothing
+    for (int i = 0; i < N; ++i) b.w[i] = uint4{0u, 0u, 0u, 0u};
   }
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, __builtin_fabsf(v[i]));
-  amax = group16_max(amax);
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, __builtin_fabsf(q1_value(b, i)));
+  amax = wave_max(amax);
+  if ((t & 63) == 0) wmax[t >> 6] = amax;
+  __syncthreads();
+  amax = wmax[0];
+#pragma unroll
+  for (int w = 1; w < 16; ++w) amax = fmaxf(amax, wmax[w]);
   const float s = scale_of(amax);
   const ScaleNorm sn = scale_norm(s);
-  if (valid) {
-    uint32_t lo = 0, hi = 0;
+  const FastScale fs = fast_scale(sn);
+  if (m < p.M) {
+    bool flag = !fs.ok;
+    uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= e4m3_code(v[i], sn) << (8 * i);
+    for (int j = 0; j < 4; ++j)
+      w[j] = fast_codes4(q1_value(b, 4 * j), q1_value(b, 4 * j + 1), q1_value(b, 4 * j + 2),
+                         q1_value(b, 4 * j + 3), fs, flag);
+    if (flag) {                                   // rare: redo this thread's codes exactly
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= e4m3_code(v[4 + i], sn) << (8 * i);
-    *reinterpret_cast<uint2*>(p.Q + e0) = uint2{lo, hi};
-    if ((lane & 15) == 0) p.S[b] = s;
+      for (int j = 0; j < 4; ++j)
+        w[j] = exact_codes4(q1_value(b, 4 * j), q1_value(b, 4 * j + 1), q1_value(b, 4 * j + 2),
+                            q1_value(b, 4 * j + 3), sn);
+    }
+    *reinterpret_cast<uint4*>(p.Q + e0) = uint4{w[0], w[1], w[2], w[3]};
   }
+  if (t == 0) p.S[size_t(rb) * Kb + kb] = s;
 }
 
-#define DG_QUANT_KERNEL_DEF(NAME, BODY, BF16) \
-  __global__ __launch_bounds__(256) void NAME(QuantArgs p) { BODY<BF16>(p); }
-#define DG_QUANT_KERNEL_DECL(NAME, BODY, BF16) __global__ __launch_bounds__(256) void NAME(QuantArgs p);
-DG_KERNEL(DG_QUANT_KERNEL, MISC)(dg_quant_128x128_bf16, quant128_body, true)
-DG_KERNEL(DG_QUANT_KERNEL, MISC)(dg_quant_128x128_f32, quant128_body, false)
-DG_KERNEL(DG_QUANT_KERNEL, MISC)(dg_quant_1x128_bf16, quant1_body, true)
-DG_KERNEL(DG_QUANT_KERNEL, MISC)(dg_quant_1x128_f32, quant1_body, false)
+#define DG_QUANT_KERNEL_DEF(NAME, BODY, BF16, THREADS) \
+  __global__ __launch_bounds__(THREADS) void NAME(QuantArgs p) { BODY<BF16>(p); }
+#define DG_QUANT_KERNEL_DECL(NAME, BODY, BF16, THREADS) __global__ __launch_bounds__(THREADS) void NAME(QuantArgs p);
+DG_KERNEL(DG_QUANT_KERNEL, MISC)(dg_quant_128x128_bf16, quant128_body, true, 1024)
+DG_KERNEL(DG_QUANT_KERNEL, MISC)(dg_quant_128x128_f32, quant128_body, false, 1024)
+DG_KERNEL(DG_QUANT_KERNEL, MISC)(dg_quant_1x128_bf16, quant1_body, true, 256)
+DG_KERNEL(DG_QUANT_KERNEL, MISC)(dg_quant_1x128_f32, quant1_body, false, 256)
 #undef DG_QUANT_KERNEL_DECL
 #undef DG_QUANT_KERNEL_DEF
 
