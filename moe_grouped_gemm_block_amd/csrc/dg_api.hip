@@ -47,18 +47,18 @@ int check_common(const void* A, const float* sA, const void* B, const float* sB,
   return DG_OK;
 }
 
-// Tile shape of one launch.  The 128 x 512 tile runs 8 waves of 64 x 128
-// (two per SIMD, one workgroup per CU, 160 KB of LDS); the 256 x 256 tile
-// (8 waves of 64 x 128, 128 KB of LDS) computes bit-identical results to
-// 128 x 512, copies 20 % fewer bytes per K-block and takes dense problems
-// whose 256 x 256 tiles fill whole rounds of the CUs (4096^3, 8192^2 x K, ...).
+// Tile shape of one launch.  Dense problems whose 256 x 256 tiles fill whole
+// rounds of the CUs (4096^3, 8192^2 x K, ...) run on the shared-B 256 x 256
+// tile (gemm_sharedb.hpp: 8 waves of 32 x 256, B converted once per
+// workgroup into LDS).  Otherwise the 128 x 512 tile runs 8 waves of 64 x 128
+// (two per SIMD, one workgroup per CU, 160 KB of LDS).
 // Narrow problems and the last partial round of a large one run on the
 // narrow tiles chosen by launch_narrow: 128 x 256 (4 waves of 64 x 128 or 8
 // of 64 x 64), 128 x 128 (4 waves of 64 x 64) or 128 x 64 (2 waves of
 // 64 x 64).
 // DG_FORCE_TILE=512 or 256 uses that tile for every problem (few rows
-// included), 3256 the shared-B 256 x 256 tile (gemm_sharedb.hpp) and 2256
-// the 256 x 256 tile of gemm_f16mma.hpp for every dense problem, and 8256 /
+// included), 3256 the shared-B 256 x 256 tile for every dense problem, and
+// 8256 /
 // 4128 / 264 the 8-wave 128 x 256 / 4-wave 128 x 128 / 2-wave 128 x 64 tile
 // wherever a narrow tile is used; DG_TAIL_TILE=0 / 256 / 8256 switches off
 // the separate last round or sets its tile (256: launch_narrow's choice;
@@ -144,12 +144,11 @@ typedef void (*kfn)(dg::GemmArgs);
 
 // Kernels of one pair of operand formats; combo = 2 * a_fmt + b_fmt.  The
 // *rs kernels take one A scale per row (1 x 128 blocks).
-struct TiledSet { kfn sb256[2], k512[2], k256[2], k256sq[2], k256w8[2], k128w4[2], k64w2[2]; };   // [f32, bf16]
+struct TiledSet { kfn sb256[2], k512[2], k256[2], k256w8[2], k128w4[2], k64w2[2]; };   // [f32, bf16]
 #define DG_TILED_SET(SFX)                                                   \
   {{dg::dg_gemm_sb256_f32##SFX, dg::dg_gemm_sb256_bf16##SFX},               \
    {dg::dg_gemm_128x512_f32##SFX, dg::dg_gemm_128x512_bf16##SFX},           \
    {dg::dg_gemm_128x256_f32##SFX, dg::dg_gemm_128x256_bf16##SFX},           \
-   {dg::dg_gemm_256x256_f32##SFX, dg::dg_gemm_256x256_bf16##SFX},           \
    {dg::dg_gemm_128x256w8_f32##SFX, dg::dg_gemm_128x256w8_bf16##SFX},       \
    {dg::dg_gemm_128x128w4_f32##SFX, dg::dg_gemm_128x128w4_bf16##SFX},       \
    {dg::dg_gemm_128x64w2_f32##SFX, dg::dg_gemm_128x64w2_bf16##SFX}}
@@ -293,8 +292,6 @@ int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, int row_s
     // tile whose eight waves share one FP16 copy of B
     if (forced_tile() == 3256 || (forced_tile() == 0 && a.M % 256 == 0 && t256 % num_cus() == 0))
       return launch_tiles(a, 256, 512, ks.sb256[1], ks.sb256[0], out_dtype, stream, 0, int(m256));
-    if (forced_tile() == 2256)
-      return launch_tiles(a, 256, 512, ks.k256sq[1], ks.k256sq[0], out_dtype, stream, 0, int(m256));
   }
   if (use512 && forced_tile() == 0 && tail_tile() != 0) {
     // A 128 x 512 tile takes about as long whether 1 or all 256 CUs are busy,

@@ -540,11 +540,7 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   }
 }
 
-// Named kernels (one per tile shape and output type) around the body.  The
-// 256 x 256 tile (4 x 2 waves) does the same work per wave as 128 x 512 with
-// 20 % fewer bytes copied into LDS per K-block (64 KB instead of 80 KB); its
-// 256-row tiles would straddle 128-row expert segments, so it serves dense
-// problems only.
+// Named kernels (one per tile shape and output type) around the body.
 // One named kernel per tile shape, output type and pair of operand formats
 // (suffix _a<A format>b<B format>, 4 = E4M3, 5 = E5M2; E4M3 x E4M3 keeps the
 // plain name); suffix _rs: row-scaled A (1 x 128 scales).
@@ -559,13 +555,11 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   K(dg_gemm_##SHAPE##_f32##SFX, NWM, NWN, WN, false, FA, FB, RS)
 #define DG_GEMM_FORMATS(K, SFX, FA, FB)                                     \
   DG_GEMM_SHAPE(K, 128x512, 2, 4, 128, SFX, FA, FB, false)                  \
-  DG_GEMM_SHAPE(K, 256x256, 4, 2, 128, SFX, FA, FB, false)                  \
   DG_GEMM_SHAPE(K, 128x256, 2, 2, 128, SFX, FA, FB, false)                  \
   DG_GEMM_SHAPE(K, 128x256w8, 2, 4, 64, SFX, FA, FB, false)                 \
   DG_GEMM_SHAPE(K, 128x128w4, 2, 2, 64, SFX, FA, FB, false)                 \
   DG_GEMM_SHAPE(K, 128x64w2, 2, 1, 64, SFX, FA, FB, false)                  \
   DG_GEMM_SHAPE(K, 128x512, 2, 4, 128, SFX##_rs, FA, FB, true)              \
-  DG_GEMM_SHAPE(K, 256x256, 4, 2, 128, SFX##_rs, FA, FB, true)              \
   DG_GEMM_SHAPE(K, 128x256, 2, 2, 128, SFX##_rs, FA, FB, true)              \
   DG_GEMM_SHAPE(K, 128x256w8, 2, 4, 64, SFX##_rs, FA, FB, true)             \
   DG_GEMM_SHAPE(K, 128x128w4, 2, 2, 64, SFX##_rs, FA, FB, true)             \

@@ -64,7 +64,7 @@ def test_e4m3_gemm_kernels_do_not_spill():
     gemm = {k: v for k, v in sizes.items()
             if re.search(r"dg_(gemm|skinny|segments)_", k) and not any(f in k for f in OTHER_FORMATS)}
     # tiled shapes (with and without row scales), few-rows and packed-segment kernels
-    for shape in ("128x512", "256x256", "128x256", "128x256w8", "128x128", "128x128w4", "128x64w2", "skinny_m64",
+    for shape in ("sb256", "128x512", "128x256", "128x256w8", "128x128w4", "128x64w2", "skinny_m64",
                   "segments_n48"):
         assert any(shape in k for k in gemm), f"no {shape} kernel found"
     spilled = {k: v for k, v in gemm.items() if v != 0}

@@ -1,6 +1,6 @@
 """The tile-choice overrides (DG_FORCE_TILE: 512 / 256 = one tile shape for
-every problem, 3256 / 2256 = the shared-B / the per-wave-conversion 256 x 256
-tile for every dense problem, 8256 /
+every problem, 3256 = the shared-B 256 x 256 tile for every dense problem,
+8256 /
 4128 / 264 = one narrow tile wherever a narrow tile is used; DG_TAIL_TILE:
 0 = no separate last round, 8256 = the 8-wave 128 x 256 tile for it) give
 results inside the parity bound.  The library reads them once per process, so every setting
@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 @pytest.mark.parametrize("env", [{"DG_FORCE_TILE": "512"}, {"DG_FORCE_TILE": "3256"},
-                                 {"DG_FORCE_TILE": "2256"}, {"DG_FORCE_TILE": "8256"},
+                                 {"DG_FORCE_TILE": "8256"},
                                  {"DG_FORCE_TILE": "4128"}, {"DG_FORCE_TILE": "264"},
                                  {"DG_TAIL_TILE": "8256"},
                                  {"DG_FORCE_TILE": "256"}, {"DG_TAIL_TILE": "0"}],
