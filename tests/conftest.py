@@ -23,9 +23,11 @@ def pytest_terminal_summary(terminalreporter):
     cases closest to the bound."""
     import parity_log
     rows = parity_log.RATIOS
+    tr = terminalreporter
+    for n in parity_log.NOTES:
+        tr.write_line(n)
     if not rows:
         return
-    tr = terminalreporter
     full = [r for r in rows if r[0].startswith("workload")]
     worst = sorted(rows, key=lambda r: -r[1])[:10]
     tr.write_line(f"parity: {len(rows)} comparisons, max err/bound {max(r[1] for r in rows):.3g}")

@@ -93,9 +93,11 @@ def test_fp8_matrix_cores_drop_small_products():
 
     Cv = vendor_fp8(A8, B8)
     lost = exact[same] - Cv[same]
-    log(f"  crafted groups: exact {exact[same][0]:.0f}, vendor FP8 GEMM {Cv[same][0]:.0f} "
-        f"(lost {lost.min():.0f} .. {lost.max():.0f} of {groups * 28} in small products), this library "
-        f"{Cd[same][0]:.0f}")
+    msg = (f"crafted FP8 groups (2^16 + 7 x 2^2 per group of 8, {groups} groups): exact {exact[same][0]:.0f}, "
+           f"vendor FP8 GEMM {Cv[same][0]:.0f} (lost {lost.min():.0f} .. {lost.max():.0f} of {groups * 28}), "
+           f"this library {Cd[same][0]:.0f}")
+    log("  " + msg)
+    parity_log.note(msg)
     # every output whose groups pair 2^16 with 2^2 loses small products (all
     # of them when each product is cut to the window, part of them when the
     # small ones are summed first), never more, and the rest is exact
@@ -118,4 +120,6 @@ def test_fp8_matrix_core_accumulation_vs_this_library(M, N, K):
     rd = float((np.abs(Cd - Cr) / bound).max())
     log(f"  {M}x{N}x{K} FP32 out: vendor FP8 GEMM max err/bound = {rv:.3g}, this library = {rd:.3g}")
     parity_log.record(f"vendor-comparison {M}x{N}x{K} f32 (vendor FP8 GEMM: {rv:.3g})", rd)
+    parity_log.note(f"Gaussian E4M3 {M}x{N}x{K}, unit scales, FP32 out: max err/bound vendor FP8 GEMM {rv:.3g}, "
+                    f"this library {rd:.3g}")
     assert rd <= 1.0
