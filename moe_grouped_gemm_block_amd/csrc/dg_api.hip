@@ -8,6 +8,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "dg.h"
@@ -122,21 +123,103 @@ int check_offsets(const int32_t* offs, int G, int64_t M_total, bool padded, hipS
   return DG_OK;
 }
 
+// ---- split-K workspace -------------------------------------------------------
+// A launch with fewer workgroups than CUs leaves the rest of the chip idle;
+// splitting K over several copies of its tile grid fills it, at the price of
+// writing FP32 partial tiles and adding them up in a second kernel (in a fixed
+// order, so the result does not depend on scheduling).  The partials live in
+// a workspace of kWsBytes per (device, stream), allocated by the first call
+// on that stream that splits and kept until the process ends (a graph
+// captured on the stream refers to it).  Calls on one stream are ordered, so
+// they share it safely; calls on different streams use different
+// workspaces.  A graph captured on a stream uses that stream's workspace
+// when it is replayed: replays that overlap other calls made on the capture
+// stream, or other replays of graphs captured on it, race.
+// The allocation is made even while the stream is being captured (this
+// thread's capture mode is switched to relaxed around hipMalloc, which
+// enqueues nothing), so that a call computes the same result captured or
+// not; only if the allocation fails does the call run unsplit.
+constexpr size_t kWsBytes = size_t(32) << 20;
+
+struct Workspace {
+  int dev;
+  hipStream_t stream;
+  float* p;
+};
+
+float* stream_workspace(hipStream_t stream) {
+  static std::mutex mu;
+  static std::vector<Workspace> all;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Workspace& w : all)
+    if (w.dev == dev && w.stream == stream) return w.p;
+  hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+  if (hipThreadExchangeStreamCaptureMode(&mode) != hipSuccess) return nullptr;
+  void* p = nullptr;
+  const hipError_t err = hipMalloc(&p, kWsBytes);
+  (void)hipThreadExchangeStreamCaptureMode(&mode);   // back to the caller's mode
+  if (err != hipSuccess) {
+    (void)hipGetLastError();   // leave no sticky error behind: the call runs unsplit
+    return nullptr;
+  }
+  all.push_back({dev, stream, static_cast<float*>(p)});
+  return static_cast<float*>(p);
+}
+
+// DG_SPLITK (read once): unset or 0 = automatic, 1 = never split, S > 1 =
+// split every launch of the tiled kernels into S parts (tuning aid).
+int splitk_override() {
+  static const int v = [] {
+    const char* e = getenv("DG_SPLITK");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
 // One launch over the row tiles [m_tile0, m_tile0 + m_tiles) of the kernel's
 // tile height (128 rows unless stated; m_tiles < 0: all 128-row tiles).
+// `splittable`: the kernels take a split of K (gemm_f16mma.hpp); the launch
+// then splits K `splits` ways (DG_SPLITK > 1 overrides), fewer if the
+// partials would not fit the workspace, none without a workspace.
 int launch_tiles(dg::GemmArgs a, int bn, int threads, void (*k_bf16)(dg::GemmArgs),
                  void (*k_f32)(dg::GemmArgs), int out_dtype, hipStream_t stream, int m_tile0 = 0,
-                 int m_tiles = -1) {
+                 int m_tiles = -1, bool splittable = true, int splits = 1) {
   a.m_tile0 = m_tile0;
   a.m_tiles = m_tiles >= 0 ? m_tiles : int((int64_t(a.M) + 127) / 128);
   a.n_tiles = int((int64_t(a.N) + bn - 1) / bn);
+  a.splits = 1;
   const int64_t blocks = int64_t(a.m_tiles) * a.n_tiles;
   if (blocks <= 0) return DG_OK;
   if (blocks > INT32_MAX) return DG_ERR_UNSUPPORTED;
+  const int64_t row0 = int64_t(m_tile0) * 128;
+  const int64_t rows = std::min<int64_t>(int64_t(a.M) - row0, int64_t(a.m_tiles) * 128);
+  int S = !splittable ? 1 : splitk_override() > 1 ? splitk_override() : splitk_override() == 1 ? 1 : splits;
+  const int64_t plane = rows * ((int64_t(a.N) + 3) / 4 * 4) * 4;
+  while (S > 1 && int64_t(S) * plane > int64_t(kWsBytes)) --S;
+  if (S > 1) {
+    a.ws = stream_workspace(stream);
+    if (a.ws == nullptr) S = 1;
+  }
+  if (S > 1 && (blocks * S > INT32_MAX || rows * ((int64_t(a.N) + 7) / 8) > INT32_MAX)) S = 1;
+  if (S > 1) {
+    a.splits = S;
+    a.ws_ld = int((int64_t(a.N) + 3) / 4 * 4);
+    a.ws_rows = int(rows);
+  }
   void* kargs[] = {&a};
   const void* fn = out_dtype == DG_OUT_BF16 ? reinterpret_cast<const void*>(k_bf16)
                                             : reinterpret_cast<const void*>(k_f32);
-  hipError_t err = hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(threads), kargs, 0, stream);
+  hipError_t err = hipLaunchKernel(fn, dim3(unsigned(blocks * S)), dim3(threads), kargs, 0, stream);
+  if (err != hipSuccess) return DG_ERR_LAUNCH;
+  if (S == 1) return DG_OK;
+  dg::ReduceArgs r{a.ws, a.C, S, int(rows), a.N, a.ws_ld, int(row0)};
+  const int64_t threads_r = rows * ((int64_t(a.N) + 7) / 8);
+  void* rargs[] = {&r};
+  const void* rfn = out_dtype == DG_OUT_BF16 ? reinterpret_cast<const void*>(dg::dg_splitk_reduce_bf16)
+                                             : reinterpret_cast<const void*>(dg::dg_splitk_reduce_f32);
+  err = hipLaunchKernel(rfn, dim3(unsigned((threads_r + 255) / 256)), dim3(256), rargs, 0, stream);
   return err == hipSuccess ? DG_OK : DG_ERR_LAUNCH;
 }
 
@@ -251,11 +334,30 @@ int best_narrow(int64_t rows, int64_t N, double* est = nullptr) {
   return best;
 }
 
+// Splits of K for `rows` row tiles x N columns on the 128 x 128 tile: as
+// many copies of its grid as fit whole into one round of the CUs, at most 8,
+// each with at least 8 K-blocks (below that the partials' write-out and the
+// separate sum, ~5 us per launch, cost more than the idle CUs).  Measured
+// (MI355X, K = 4096, BF16 out, graph replay; best narrow tile unsplit ->
+// split): 128 x 4096 35.4 -> 20.2 us (4 splits), 256 x 4096 35.4 -> 22.6 us
+// (4), 512 x 4096 35.7 -> 29.9 us (2), 128 x 12288 35.9 -> ~28 us (2);
+// 256 x 4096 x 1024 (8 K-blocks) 11.3 us unsplit, 15 us split 2 ways.
+int narrow_splits(int64_t rows, int64_t N, int Kb) {
+  const int64_t tiles = rows * ((N + 127) / 128);
+  if (tiles <= 0) return 1;
+  return int(std::max<int64_t>(1, std::min<int64_t>({int64_t(num_cus()) / tiles, int64_t(Kb / 8), int64_t(8)})));
+}
+
 // The row tiles [m_tile0, m_tile0 + m_tiles) (all when m_tiles < 0) on the
-// narrow tile with the least estimated time (or the one an override names).
+// narrow tile with the least estimated time (or the one an override names),
+// or split over K on the 128 x 128 tile when that fills idle CUs.
 int launch_narrow(const dg::GemmArgs& a, const TiledSet& ks, int out_dtype, hipStream_t stream, int m_tile0 = 0,
                   int m_tiles = -1) {
   const int64_t rows = m_tiles >= 0 ? m_tiles : (int64_t(a.M) + 127) / 128;
+  const int Kb = int((int64_t(a.K) + dg::KBLK - 1) / dg::KBLK);
+  const int S = forced_tile() == 0 && splitk_override() == 0 ? narrow_splits(rows, a.N, Kb) : 1;
+  if (S > 1)
+    return launch_tiles(a, 128, 256, ks.k128w4[1], ks.k128w4[0], out_dtype, stream, m_tile0, m_tiles, true, S);
   int t = best_narrow(rows, a.N);
   if (forced_tile() == 256) t = kN256w4;
   if (forced_tile() == 8256 || tail_tile() == 8256) t = kN256w8;
@@ -291,7 +393,7 @@ int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, int row_s
     // dense problems whose 256 x 256 tiles fill whole rounds of the CUs: the
     // tile whose eight waves share one FP16 copy of B
     if (forced_tile() == 3256 || (forced_tile() == 0 && a.M % 256 == 0 && t256 % num_cus() == 0))
-      return launch_tiles(a, 256, 512, ks.sb256[1], ks.sb256[0], out_dtype, stream, 0, int(m256));
+      return launch_tiles(a, 256, 512, ks.sb256[1], ks.sb256[0], out_dtype, stream, 0, int(m256), false);
   }
   if (use512 && forced_tile() == 0 && tail_tile() != 0) {
     // A 128 x 512 tile takes about as long whether 1 or all 256 CUs are busy,

@@ -191,7 +191,20 @@ struct GemmArgs {
   int M, N, K;
   int m_tiles, n_tiles;    // tiles of this launch
   int m_tile0;            // first row tile of this launch, in tiles of the kernel's height (a launch may cover a row range)
+  // Split K (tiled kernels only): with splits > 1 the grid holds `splits`
+  // copies of the tile grid; copy s sums K-blocks [s Kb / splits,
+  // (s + 1) Kb / splits) of every tile and stores its FP32 partial into
+  // ws[s][row - m_tile0 * tile height][column] (row stride ws_ld, a
+  // multiple of 4 that is at least N; ws_rows rows per copy) instead of C.
+  // splitk_reduce then adds the copies in order s = 0, 1, ... into C.
+  int splits;
+  float* ws;
+  int ws_ld, ws_rows;
 };
+
+// K-blocks [kb_begin, kb_end) of split s out of S (every split gets
+// floor or ceil of Kb / S; a split may be empty when S > Kb).
+__device__ __forceinline__ int split_kb(int s, int S, int Kb) { return int((int64_t(s) * Kb) / S); }
 
 // Tile order: blockIdx -> (m-tile, n-tile).  Workgroups are dealt to the 8
 // XCDs round-robin (block b runs on XCD b % 8), so block b is given tile t
@@ -238,12 +251,17 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // split of K this workgroup sums (0 without a split) and its tile
+  const int T = p.m_tiles * p.n_tiles;
+  const int split = p.splits > 1 ? int(blockIdx.x) / T : 0;
   int tm, tn;
-  tile_of<8>(blockIdx.x, p.m_tiles, p.n_tiles, tm, tn);
+  tile_of<8>(int(blockIdx.x) - split * T, p.m_tiles, p.n_tiles, tm, tn);
   const int m0 = (p.m_tile0 + tm) * BM, n0 = tn * BN;
   const int M = p.M, N = p.N, K = p.K;
   const int Kb = (K + KBLK - 1) / KBLK;          // the last K-block may be partial
   const int Nb = (N + KBLK - 1) / KBLK;
+  const int S = max(p.splits, 1);
+  const int kb0 = split_kb(split, S, Kb), kb1 = split_kb(split + 1, S, Kb);
 
   int e = 0;
   if (p.offs != nullptr) {
@@ -319,8 +337,8 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   const int b_off0 = (wn + r16) * KBLK + swz16(r16, 2 * q) * 16;
   const int b_off1 = (wn + r16) * KBLK + swz16(r16, 2 * q + 1) * 16;
 
-  if (Kb > 0) {
-    issue_copies(0, 0);
+  if (kb1 > kb0) {
+    issue_copies(kb0, 0);
     wait_vmem();
     __syncthreads();
   }
@@ -338,12 +356,12 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
     sa_lane = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rS, int(s_off + uint32_t(kb * 4)), 0, 0));
   };
   if constexpr (ROW_SA) {
-    if (Kb > 0) load_row_scales(0);
+    if (kb1 > kb0) load_row_scales(kb0);
   }
 
-  float sa_next = Kb > 0 && !ROW_SA ? float(sAr[0]) : 1.f, sb_next = Kb > 0 ? sBr[0] : 0.f;
-  for (int kb = 0; kb < Kb; ++kb) {
-    const int stage = kb & 1;
+  float sa_next = kb1 > kb0 && !ROW_SA ? float(sAr[kb0]) : 1.f, sb_next = kb1 > kb0 ? sBr[kb0] : 0.f;
+  for (int kb = kb0; kb < kb1; ++kb) {
+    const int stage = (kb - kb0) & 1;
     const float s = sa_next * sb_next;         // this K-block's fp32(sA * sB)
     float s_m[MI];                              // the factor of row group mi
 #pragma unroll
@@ -359,7 +377,7 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
         asm volatile("" : "+v"(s_m[mi]));
       }
     }
-    if (kb + 1 < Kb) {
+    if (kb + 1 < kb1) {
       if constexpr (ROW_SA) load_row_scales(kb + 1);   // prefetched one K-block ahead
       else sa_next = sAr[kb + 1];
       sb_next = sBr[kb + 1];
@@ -523,6 +541,30 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   // C[m][n0 + wn + 32 j + 8 q + 0 .. 7] ------------------------------------
   const int lane_e = lane_id();
   const int q_e = lane_e >> 4, r16_e = lane_e & 15;
+  if (p.splits > 1) {
+    // FP32 partial of this split: rows counted from the launch's first row;
+    // a vector that starts below N lies inside the padded row (ws_ld >= N
+    // rounded up to 4), so whole 16-byte vectors are stored
+    float* W = p.ws + (size_t)split * p.ws_rows * p.ws_ld;
+    const int r0 = p.m_tile0 * BM;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int m = m0 + wm + mi * 16 + r16_e;
+      if (m >= M) continue;
+      float* row = W + (size_t)(m - r0) * p.ws_ld;
+#pragma unroll
+      for (int j = 0; j < NI / 2; ++j) {
+        const int n = n0 + wn + 32 * j + 8 * q_e;
+        if (n < N)
+          *reinterpret_cast<float4*>(row + n) =
+              float4{acc[mi][2 * j][0], acc[mi][2 * j][1], acc[mi][2 * j][2], acc[mi][2 * j][3]};
+        if (n + 4 < N)
+          *reinterpret_cast<float4*>(row + n + 4) =
+              float4{acc[mi][2 * j + 1][0], acc[mi][2 * j + 1][1], acc[mi][2 * j + 1][2], acc[mi][2 * j + 1][3]};
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
     const int m = m0 + wm + mi * 16 + r16_e;
@@ -538,6 +580,41 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
       store_row_span<OUT_BF16, 8>(p.C, size_t(m) * N, n0 + wn + 32 * j + 8 * q_e, N, v);
     }
   }
+}
+
+// Sum of the split-K partials: C[row0 + r][n] = ((ws[0][r][n] + ws[1][r][n])
+// + ...) + ws[S-1][r][n], always in this order (the result does not depend
+// on which split finished first), rounded once to the output type.  One
+// thread per 8 consecutive columns of a row.
+struct ReduceArgs {
+  const float* ws;   // [splits][rows][ld]
+  void* C;           // [..][N]; rows row0 .. row0 + rows - 1 are written
+  int splits, rows, N, ld, row0;
+};
+
+template <bool OUT_BF16>
+__device__ __forceinline__ void splitk_reduce_body(const ReduceArgs& a) {
+  const int chunks = (a.N + 7) / 8;
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= int64_t(a.rows) * chunks) return;
+  const int r = int(idx / chunks);
+  const int n = int(idx - int64_t(r) * chunks) * 8;
+  const bool hi = n + 4 < a.N;                     // second vector inside the row
+  const size_t plane = (size_t)a.rows * a.ld;
+  const float* src = a.ws + (size_t)r * a.ld + n;
+  float4 x0 = *reinterpret_cast<const float4*>(src);
+  float4 x1 = hi ? *reinterpret_cast<const float4*>(src + 4) : float4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 1; s < a.splits; ++s) {
+    const float* t = src + s * plane;
+    const float4 y0 = *reinterpret_cast<const float4*>(t);
+    x0.x += y0.x; x0.y += y0.y; x0.z += y0.z; x0.w += y0.w;
+    if (hi) {
+      const float4 y1 = *reinterpret_cast<const float4*>(t + 4);
+      x1.x += y1.x; x1.y += y1.y; x1.z += y1.z; x1.w += y1.w;
+    }
+  }
+  const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  store_row_span<OUT_BF16, 8>(a.C, size_t(a.row0 + r) * a.N, n, a.N, v);
 }
 
 // Named kernels (one per tile shape and output type) around the body.
@@ -572,5 +649,13 @@ DG_GEMM_FORMATS(DG_KERNEL(DG_GEMM_KERNEL, FMT_54), _a5b4, FMT_E5M2, FMT_E4M3)
 #undef DG_GEMM_SHAPE
 #undef DG_GEMM_KERNEL_DECL
 #undef DG_GEMM_KERNEL_DEF
+
+#define DG_REDUCE_KERNEL_DEF(NAME, BF16) \
+  __global__ __launch_bounds__(256) void NAME(ReduceArgs a) { splitk_reduce_body<BF16>(a); }
+#define DG_REDUCE_KERNEL_DECL(NAME, BF16) __global__ __launch_bounds__(256) void NAME(ReduceArgs a);
+DG_KERNEL(DG_REDUCE_KERNEL, MISC)(dg_splitk_reduce_bf16, true)
+DG_KERNEL(DG_REDUCE_KERNEL, MISC)(dg_splitk_reduce_f32, false)
+#undef DG_REDUCE_KERNEL_DECL
+#undef DG_REDUCE_KERNEL_DEF
 
 }  // namespace dg

@@ -1,6 +1,6 @@
 """Child process of tests/test_gpu_overrides.py (not collected by pytest).
 
-The library reads DG_FORCE_TILE and DG_TAIL_TILE once per process, so each
+The library reads DG_FORCE_TILE, DG_TAIL_TILE and DG_SPLITK once per process, so each
 setting is checked in a process of its own: a few dense and grouped GEMMs
 through the C-ABI against the CPU oracle, with the same tolerance as the
 parity tests.  Exit status 0 when every case is inside it."""
@@ -29,7 +29,7 @@ def ratio(Cg, Cr, mass, out):
 
 
 def main():
-    setting = {k: os.environ.get(k) for k in ("DG_FORCE_TILE", "DG_TAIL_TILE")}
+    setting = {k: os.environ.get(k) for k in ("DG_FORCE_TILE", "DG_TAIL_TILE", "DG_SPLITK")}
     print(f"override child {setting}", flush=True)
     worst = 0.0
     # dense: ragged, and a grid with a partial last round of 128 x 512 tiles
