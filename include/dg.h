@@ -31,9 +31,25 @@
  *   C  : [M][N] row-major, float32 or bfloat16 (out_dtype)
  *
  * Conventions shared by every entry point:
- *   - All data pointers are device memory owned by the caller.  The library
- *     allocates nothing and keeps no per-call state: calls are thread-safe and
- *     may run concurrently on different streams.
+ *   - All data pointers are device memory owned by the caller.  The only
+ *     memory the library allocates is the split-K workspace (next item);
+ *     there is no other per-call state: calls are thread-safe and may run
+ *     concurrently on different streams.
+ *   - Split K.  A GEMM whose 128-row output tiles would occupy at most half
+ *     of the GPU's compute units, with at least 16 K-blocks, is computed as S
+ *     (2..8) partial GEMMs over consecutive ranges of K-blocks, each summed
+ *     and rescaled per K-block exactly as above into FP32, then added in the
+ *     order of their ranges: C = sum_s (sum_{kb in range s} fp32(sA sB) P_kb),
+ *     one rounding to out_dtype at the end.  The FP32 partials live in a
+ *     workspace of 32 MB per (device, stream), allocated by the first call
+ *     on that stream that splits (also while the stream is being captured
+ *     into a graph: the allocation is made in relaxed capture mode and
+ *     enqueues nothing) and kept until the process ends.  Calls on one
+ *     stream share it in stream order; calls on different streams use
+ *     different workspaces.  A graph captured on a stream uses that
+ *     stream's workspace whenever it is replayed: replays must not overlap
+ *     other calls made on the capture stream or other replays of graphs
+ *     captured on it.  If the allocation fails the call runs unsplit.
  *   - Calls are asynchronous: the work is enqueued on `stream` (0 = the null
  *     stream) and the call returns without synchronising.  Passing the stream
  *     explicitly lets a caller order the GEMM against collectives on the same
@@ -55,11 +71,13 @@
  *     writes zeros.
  *   - A failed kernel launch returns DG_ERR_LAUNCH.  Faults inside a kernel
  *     surface at the caller's next synchronisation, as for any HIP kernel.
- *   - Every call only enqueues kernels (no allocation, no memset, no host
- *     synchronisation), so it may be captured into a HIP graph and replayed
- *     (the DG_VALIDATE=1 debugging aid of the grouped calls excepted).
+ *   - Every call only enqueues kernels (no memset, no host synchronisation;
+ *     apart from the workspace allocation above), so it may be captured into
+ *     a HIP graph and replayed (the DG_VALIDATE=1 debugging aid of the
+ *     grouped calls excepted).
  *   - Results are bitwise repeatable: no atomics, and every output element
- *     is summed in a fixed order.
+ *     is summed in a fixed order (the split of K depends only on the shape
+ *     and the GPU's compute unit count).
  *   - Out of scope: alpha / beta (C is overwritten, alpha = 1, beta = 0),
  *     transposed layouts other than the above, other element types.
  */
