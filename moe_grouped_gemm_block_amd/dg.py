@@ -36,13 +36,25 @@ _lib = None
 
 
 def lib() -> ctypes.CDLL:
-    """Load libdg.so once; raise if it is missing."""
+    """Load libdg.so once; raise if it is missing.
+
+    torch is imported first when it is installed: torch's ROCm build carries
+    its own HIP runtime, and libdg.so's dependency on the HIP runtime is then
+    satisfied by that already-loaded copy.  Loaded the other way round, the
+    process would hold two HIP runtimes (the system one for libdg.so, torch's
+    for the tensors), and the library's runtime, initialised second, cannot
+    use the GPU (its device queries fail).
+    """
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(
                 f"{LIB_PATH} is not built; run `python -m moe_grouped_gemm_block_amd.build` "
                 "(there is no non-HIP fallback)")
+        try:
+            import torch  # noqa: F401  (one HIP runtime for torch and the library)
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.dg_gemm_fp8_blockscaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, vp]

@@ -9,6 +9,7 @@ import glob
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -195,3 +196,18 @@ def test_operand_format_follows_float8_dtype():
         dg.operand_fmt(e5, "e4m3", "A")
     with pytest.raises(ValueError):
         dg.operand_fmt(e4, dg.DG_FP8_E5M2, "B")
+
+
+def test_binding_loads_one_hip_runtime():
+    """With torch installed, the binding loads it before libdg.so, so the
+    process holds one HIP runtime (torch's ROCm build carries its own; a
+    second, system runtime initialised after it cannot use the GPU)."""
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from moe_grouped_gemm_block_amd import dg\n"
+            "dg.lib()\n"
+            "libs = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(sorted(libs))\n"
+            "sys.exit(0 if len(libs) == 1 else 1)\n") % ROOT
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stdout + r.stderr[-2000:]
+
