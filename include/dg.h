@@ -184,6 +184,32 @@ int dg_gemm_fp8_ex(const void* A, int a_fmt, const float* sA, int sa_rows,
                    void* C, int64_t M, int64_t N, int64_t K,
                    int out_dtype, hipStream_t stream);
 
+/*
+ * dg_gemm_fp8_ex for callers that cannot allocate device memory: code under
+ * HIP graph capture that must not allocate, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, layouts, result (bit for bit, when
+ * dg_gemm_fp8_ex has its workspace: the same kernels and the same split of K)
+ * and errors as dg_gemm_fp8_ex, except where the split-K partials go: a
+ * static device buffer of 32 MB that the library holds on every device it
+ * runs on until the process ends, instead of the per-stream workspace.  The
+ * call allocates nothing (no hipMalloc, no allocating library routine); the
+ * caller still provides A, B, the scales and C.
+ *
+ * The automatic split never needs more than 64 KB per compute unit of the
+ * GPU (16 MB on the MI355X); a call whose partials would exceed the buffer
+ * -- only the DG_SPLITK tuning override can ask for that -- returns
+ * DG_ERR_UNSUPPORTED before any launch.  DG_ERR_LAUNCH if the buffer's
+ * device address cannot be looked up.  Every call on a device shares that
+ * device's buffer, which keeps the last call's contents (nothing in it needs
+ * clearing: every partial is written before it is read): calls that overlap
+ * in time on one device -- on different streams, or replays of captured
+ * graphs -- race and give undefined results.
+ */
+int dg_gemm_fp8_ex_noalloc(const void* A, int a_fmt, const float* sA, int sa_rows,
+                           const void* B, int b_fmt, const float* sB,
+                           void* C, int64_t M, int64_t N, int64_t K,
+                           int out_dtype, hipStream_t stream);
+
 int dg_grouped_gemm_fp8_ex(const void* A, int a_fmt, const float* sA, int sa_rows,
                            const void* B, int b_fmt, const float* sB,
                            void* C, const int32_t* group_offsets,

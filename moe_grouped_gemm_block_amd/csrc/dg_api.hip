@@ -168,6 +168,37 @@ float* stream_workspace(hipStream_t stream) {
   return static_cast<float*>(p);
 }
 
+// ---- the static scratch of dg_gemm_fp8_ex_noalloc ---------------------------
+// For callers that cannot allocate: the split-K partials go to this array
+// (one copy per device, loaded with the library's code object and held until
+// the process ends) instead of a stream workspace.  Its size equals the
+// stream workspace's, so both calls split alike and give the same bits.
+// Every call on a device shares it: calls that overlap in time on one device
+// race.  Nothing in it needs clearing: every partial is written before it is
+// read.  In host code `scratch` is a stand-in for the device copy; kernels
+// get the address from scratch_address().
+constexpr size_t kScratchBytes = kWsBytes;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+// Device address of the current device's scratch, looked up once per device
+// (with that device current) and cached; nullptr if the lookup fails.
+float* scratch_address() {
+  static std::mutex mu;
+  static float* addr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    addr[dev] = static_cast<float*>(p);
+  }
+  return addr[dev];
+}
+
 // DG_SPLITK (read once): unset or 0 = automatic, 1 = never split, S > 1 =
 // split every launch of the tiled kernels into S parts (tuning aid).
 int splitk_override() {
@@ -182,7 +213,9 @@ int splitk_override() {
 // tile height (128 rows unless stated; m_tiles < 0: all 128-row tiles).
 // `splittable`: the kernels take a split of K (gemm_f16mma.hpp); the launch
 // then splits K `splits` ways (DG_SPLITK > 1 overrides), fewer if the
-// partials would not fit the workspace, none without a workspace.
+// partials would not fit the workspace, none without a workspace.  The
+// partials go to a.ws when the caller set it (the static scratch), else to
+// the stream's workspace.
 int launch_tiles(dg::GemmArgs a, int bn, int threads, void (*k_bf16)(dg::GemmArgs),
                  void (*k_f32)(dg::GemmArgs), int out_dtype, hipStream_t stream, int m_tile0 = 0,
                  int m_tiles = -1, bool splittable = true, int splits = 1) {
@@ -197,8 +230,9 @@ int launch_tiles(dg::GemmArgs a, int bn, int threads, void (*k_bf16)(dg::GemmArg
   const int64_t rows = std::min<int64_t>(int64_t(a.M) - row0, int64_t(a.m_tiles) * 128);
   int S = !splittable ? 1 : splitk_override() > 1 ? splitk_override() : splitk_override() == 1 ? 1 : splits;
   const int64_t plane = rows * ((int64_t(a.N) + 3) / 4 * 4) * 4;
-  while (S > 1 && int64_t(S) * plane > int64_t(kWsBytes)) --S;
-  if (S > 1) {
+  const bool preset = a.ws != nullptr;
+  while (S > 1 && int64_t(S) * plane > int64_t(preset ? kScratchBytes : kWsBytes)) --S;
+  if (S > 1 && !preset) {
     a.ws = stream_workspace(stream);
     if (a.ws == nullptr) S = 1;
   }
@@ -418,13 +452,26 @@ int launch(const dg::GemmArgs& a, int out_dtype, int a_fmt, int b_fmt, int row_s
 
 bool valid_fmt(int f) { return f == DG_FP8_E4M3 || f == DG_FP8_E5M2; }
 
+// noalloc: split-K partials go to the static scratch (dg_gemm_fp8_ex_noalloc)
 int gemm_impl(const void* A, int a_fmt, const float* sA, int sa_rows, const void* B, int b_fmt,
-              const float* sB, void* C, int64_t M, int64_t N, int64_t K, int out_dtype, hipStream_t stream) {
+              const float* sB, void* C, int64_t M, int64_t N, int64_t K, int out_dtype, hipStream_t stream,
+              bool noalloc = false) {
   if (!valid_fmt(a_fmt) || !valid_fmt(b_fmt)) return DG_ERR_INVALID_ARG;
   if (sa_rows != 128 && sa_rows != 1) return DG_ERR_INVALID_ARG;
   int st = check_common(A, sA, B, sB, C, M, N, K, out_dtype);
   if (st != DG_OK || M == 0 || N == 0) return st;
   dg::GemmArgs a{};
+  if (noalloc) {
+    // The automatic split never needs more than (compute units) x 64 KB of
+    // partials (S copies of at most CUs / S tiles of 128 x 128 FP32); only the
+    // DG_SPLITK override can ask for more than the scratch holds, and such a
+    // call is rejected here, before any launch.
+    const int64_t ld = (N + 3) / 4 * 4;
+    if (splitk_override() > 1 && int64_t(splitk_override()) * M * ld * 4 > int64_t(kScratchBytes))
+      return DG_ERR_UNSUPPORTED;
+    a.ws = scratch_address();
+    if (a.ws == nullptr) return DG_ERR_LAUNCH;
+  }
   a.A = static_cast<const uint8_t*>(A);
   a.sA = sA;
   a.B = static_cast<const uint8_t*>(B);
@@ -511,6 +558,12 @@ int dg_gemm_fp8_ex(const void* A, int a_fmt, const float* sA, int sa_rows, const
   return gemm_impl(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, M, N, K, out_dtype, stream);
 }
 
+int dg_gemm_fp8_ex_noalloc(const void* A, int a_fmt, const float* sA, int sa_rows, const void* B, int b_fmt,
+                           const float* sB, void* C, int64_t M, int64_t N, int64_t K, int out_dtype,
+                           hipStream_t stream) {
+  return gemm_impl(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, M, N, K, out_dtype, stream, true);
+}
+
 int dg_grouped_gemm_fp8_ex(const void* A, int a_fmt, const float* sA, int sa_rows, const void* B, int b_fmt,
                            const float* sB, void* C, const int32_t* group_offsets, int num_groups,
                            int64_t M_total, int64_t N, int64_t K, int out_dtype, hipStream_t stream) {
@@ -547,7 +600,8 @@ const char* dg_status_string(int status) {
     case DG_OK: return "DG_OK: success";
     case DG_ERR_INVALID_ARG: return "DG_ERR_INVALID_ARG: invalid argument (null, misaligned, negative or oversized)";
     case DG_ERR_UNSUPPORTED:
-      return "DG_ERR_UNSUPPORTED: shape not supported (GEMM: K % 16 != 0 or K > 2^22; quantiser: K % 128 != 0)";
+      return "DG_ERR_UNSUPPORTED: shape not supported (GEMM: K % 16 != 0 or K > 2^22; quantiser: K % 128 != 0; "
+             "dg_gemm_fp8_ex_noalloc: split-K partials larger than its 32 MB static scratch)";
     case DG_ERR_LAUNCH: return "DG_ERR_LAUNCH: kernel launch failed";
     default: return "unknown dg_status";
   }

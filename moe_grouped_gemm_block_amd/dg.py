@@ -28,7 +28,7 @@ DG_ERR_INVALID_ARG = -1
 DG_ERR_UNSUPPORTED = -2
 DG_ERR_LAUNCH = -3
 
-EXPORTED = ("dg_gemm_fp8_blockscaled", "dg_grouped_gemm_fp8", "dg_gemm_fp8_ex",
+EXPORTED = ("dg_gemm_fp8_blockscaled", "dg_grouped_gemm_fp8", "dg_gemm_fp8_ex", "dg_gemm_fp8_ex_noalloc",
             "dg_grouped_gemm_fp8_ex", "dg_grouped_gemm_fp8_segments", "dg_quantize_fp8_blockscaled",
             "dg_status_string")
 
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.dg_grouped_gemm_fp8.restype = ci
         L.dg_gemm_fp8_ex.argtypes = [vp, ci, vp, ci, vp, ci, vp, vp, i64, i64, i64, ci, vp]
         L.dg_gemm_fp8_ex.restype = ci
+        L.dg_gemm_fp8_ex_noalloc.argtypes = [vp, ci, vp, ci, vp, ci, vp, vp, i64, i64, i64, ci, vp]
+        L.dg_gemm_fp8_ex_noalloc.restype = ci
         L.dg_grouped_gemm_fp8_ex.argtypes = [vp, ci, vp, ci, vp, ci, vp, vp, vp, ci, i64, i64, i64, ci, vp]
         L.dg_grouped_gemm_fp8_ex.restype = ci
         L.dg_grouped_gemm_fp8_segments.argtypes = [vp, ci, vp, vp, ci, vp, vp, vp, ci, i64, i64, i64, ci, vp]
@@ -89,6 +91,10 @@ def dg_grouped_gemm_fp8(A, sA, B, sB, C, group_offsets, num_groups, M_total, N, 
 
 def dg_gemm_fp8_ex(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, M, N, K, out_dtype, stream) -> int:
     return lib().dg_gemm_fp8_ex(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, M, N, K, out_dtype, stream)
+
+
+def dg_gemm_fp8_ex_noalloc(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, M, N, K, out_dtype, stream) -> int:
+    return lib().dg_gemm_fp8_ex_noalloc(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, M, N, K, out_dtype, stream)
 
 
 def dg_grouped_gemm_fp8_ex(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, group_offsets, num_groups, M_total,
