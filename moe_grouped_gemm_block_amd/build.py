@@ -22,6 +22,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdg.so")
+LIB_STAGES1 = os.path.join(PKG, "libdg_stages1.so")
 SOURCES = ["dg_api.hip", "kernels_e4m3.hip", "kernels_e4m3_e5m2.hip", "kernels_e5m2_e4m3.hip",
            "kernels_e5m2.hip"]
 ARCH = os.environ.get("DG_OFFLOAD_ARCH", "gfx950")
@@ -35,8 +36,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC)")
 
 
-def compile_command(src: str, obj: str) -> list[str]:
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c",
+def compile_command(src: str, obj: str, stages: int = 2) -> list[str]:
+    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c", f"-DDG_STAGES={stages}",
             "-Wall", "-Wno-unused-function",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             # matrix-core results in ordinary VGPRs: the FP32 rescale reads them
@@ -58,20 +59,28 @@ def _run(cmd: list[str]) -> str:
 
 
 def build(verbose: bool = True) -> str:
+    """Build libdg.so and its single-stage twin libdg_stages1.so (the same
+    library compiled with -DDG_STAGES=1: every GEMM pipeline with one LDS
+    stage, a debugging aid whose results must equal libdg.so's bit for bit);
+    returns the path of libdg.so."""
     with tempfile.TemporaryDirectory(prefix="dg_build_") as tmp:
-        objs = [os.path.join(tmp, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-        cmds = [compile_command(s, o) for s, o in zip(SOURCES, objs)]
+        jobs_list = []
+        for stages, lib in ((2, LIB), (1, LIB_STAGES1)):
+            objs = [os.path.join(tmp, f"s{stages}_" + os.path.splitext(s)[0] + ".o") for s in SOURCES]
+            jobs_list.append((lib, objs, [compile_command(s, o, stages) for s, o in zip(SOURCES, objs)]))
+        cmds = [c for _, _, cs in jobs_list for c in cs]
         if verbose:
             for c in cmds:
                 print(" ".join(c), flush=True)
         jobs = min(len(cmds), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
         with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as pool:
             warnings = list(pool.map(_run, cmds))
-        out_tmp = LIB + ".tmp"
-        warnings.append(_run(link_command(objs, out_tmp)))
+        for lib, objs, _ in jobs_list:
+            warnings.append(_run(link_command(objs, lib + ".tmp")))
     if verbose and any(w.strip() for w in warnings):
         print("\n".join(w for w in warnings if w.strip()), file=sys.stderr)
-    os.replace(out_tmp, LIB)
+    for lib, _, _ in jobs_list:
+        os.replace(lib + ".tmp", lib)
     return LIB
 
 

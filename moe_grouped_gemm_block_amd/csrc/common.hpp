@@ -13,6 +13,20 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // A and one B factor.
 constexpr int KBLK = 128;
 
+// LDS stages of the GEMM pipelines.  2 (the default): the next K-block's
+// operands stream into one stage while the current one is read from the
+// other.  1 (build with -DDG_STAGES=1, a debugging aid): every pipeline waits
+// until the current K-block has been used before it loads the next one into
+// the same stage.  The arithmetic and its order are the same, so both builds
+// give identical bits; a difference points at a race between the loads into
+// one stage and the reads of another (the "drop to a single buffer" check of
+// the DeepGEMM FP8 kernel write-up, section 6.2).
+#ifndef DG_STAGES
+#define DG_STAGES 2
+#endif
+static_assert(DG_STAGES == 1 || DG_STAGES == 2, "DG_STAGES is 1 or 2");
+constexpr bool kSingleStage = DG_STAGES == 1;
+
 // FP32 -> BF16, round to nearest even (NaN stays NaN): gfx950 converts two
 // values per instruction (v_cvt_pk_bf16_f32).
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

@@ -361,7 +361,7 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
 
   float sa_next = kb1 > kb0 && !ROW_SA ? float(sAr[kb0]) : 1.f, sb_next = kb1 > kb0 ? sBr[kb0] : 0.f;
   for (int kb = kb0; kb < kb1; ++kb) {
-    const int stage = (kb - kb0) & 1;
+    const int stage = kSingleStage ? 0 : (kb - kb0) & 1;
     const float s = sa_next * sb_next;         // this K-block's fp32(sA * sB)
     float s_m[MI];                              // the factor of row group mi
 #pragma unroll
@@ -381,7 +381,7 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
       if constexpr (ROW_SA) load_row_scales(kb + 1);   // prefetched one K-block ahead
       else sa_next = sAr[kb + 1];
       sb_next = sBr[kb + 1];
-      issue_copies(kb + 1, stage ^ 1);
+      if constexpr (!kSingleStage) issue_copies(kb + 1, stage ^ 1);
     }
     const uint8_t* la = lds + stage * A_BYTES;
     const uint8_t* lb = lds + 2 * A_BYTES + stage * B_BYTES;
@@ -533,6 +533,10 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[mi][NI - 1][r] = __builtin_fmaf(s_m[mi], part[mi][r], acc[mi][NI - 1][r]);
+    if constexpr (kSingleStage) {
+      __syncthreads();                          // every wave is done with the stage
+      if (kb + 1 < kb1) issue_copies(kb + 1, 0);
+    }
     wait_vmem();
     __syncthreads();
   }

@@ -234,7 +234,7 @@ __device__ __forceinline__ void gemm_sharedb_body(const GemmArgs& p) {
   float sa_next = Kb > 0 && !ROW_SA ? float(sAr[0]) : 1.f;
   float sb0_next = Kb > 0 ? sB0[0] : 0.f, sb1_next = Kb > 0 ? sB1[0] : 0.f;
   for (int kb = 0; kb < Kb; ++kb) {
-    const int stage = kb & 1;
+    const int stage = kSingleStage ? 0 : kb & 1;
     // this K-block's factors: [mi][column half]
     float s[MI][2];
     if constexpr (ROW_SA) {
@@ -301,8 +301,10 @@ __device__ __forceinline__ void gemm_sharedb_body(const GemmArgs& p) {
           for (int r = 0; r < 4; ++r)
             acc[mi][ni - 1][r] = __builtin_fmaf(s[mi][(ni - 1) >= NI / 2], pp[mi][r], acc[mi][ni - 1][r]);
       }
-      if (ni >= 1 && ni <= 4) convert_b(ni - 1, stage ^ 1);
-      if (ni == 4) load_b(kb + 2);
+      if constexpr (!kSingleStage) {
+        if (ni >= 1 && ni <= 4) convert_b(ni - 1, stage ^ 1);
+        if (ni == 4) load_b(kb + 2);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -310,6 +312,12 @@ __device__ __forceinline__ void gemm_sharedb_body(const GemmArgs& p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         acc[mi][NI - 1][r] = __builtin_fmaf(s[mi][1], part[(NI - 1) & 1][mi][r], acc[mi][NI - 1][r]);
+    if constexpr (kSingleStage) {
+      __syncthreads();                          // every wave is done with the stage
+#pragma unroll
+      for (int c = 0; c < 4; ++c) convert_b(c, 0);
+      load_b(kb + 2);
+    }
     __syncthreads();
   }
 

@@ -127,18 +127,25 @@ __device__ __forceinline__ void gemm_skinny_body(const SkinnyJob& p, const int n
   // B(kb_{j+2}).  A(kb_j) and B(kb_j) are complete once at most
   // B(kb_{j+1}) + A(kb_{j+1}) + B(kb_{j+2}) copies are still outstanding.
   int j = 0, bstage = 0;
-  if (wave < Kb) {
+  if (wave < Kb && !kSingleStage) {
     issue_a(wave, 0);
     issue_b(wave, 0);
     if (wave + NW < Kb) issue_b(wave + NW, 1);
   }
   for (int kb = wave; kb < Kb; kb += NW, ++j) {
-    const int astage = j & 1;
+    const int astage = kSingleStage ? 0 : j & 1;
     const float sa = ROW_SA ? 1.f : float(sAr[kb]);
     float sb[NI];
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) sb[ni] = ((cfloat*)p.sB)[(size_t)nbk[ni] * Kb + kb];
-    if (kb + 2 * NW < Kb) {
+    if constexpr (kSingleStage) {
+      // this K-block into stage 0, once the previous one's LDS reads have
+      // returned (s_waitcnt lgkmcnt(0))
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      issue_a(kb, 0);
+      issue_b(kb, 0);
+      wait_vmem_n<0>();
+    } else if (kb + 2 * NW < Kb) {
       issue_a(kb + NW, astage ^ 1);
       issue_b(kb + 2 * NW, bstage == 0 ? 2 : bstage - 1);
       wait_vmem_n<2 * B_CH + A_OPS>();
@@ -156,7 +163,7 @@ __device__ __forceinline__ void gemm_skinny_body(const SkinnyJob& p, const int n
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) sa_m[mi] = ls[16 * mi + r16];
     }
-    bstage = bstage == 2 ? 0 : bstage + 1;
+    bstage = kSingleStage ? 0 : bstage == 2 ? 0 : bstage + 1;
     v8h af[MI][4];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
