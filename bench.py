@@ -360,6 +360,9 @@ def main():
                          "reached its sustained level (0: none)")
     ap.add_argument("--a-scale", choices=["128x128", "1x128"], default="128x128",
                     help="A scale blocks of the GEMM: 128x128, or one per token and 128 columns")
+    ap.add_argument("--counts", action="store_true",
+                    help="grouped workloads: pass the real per-expert row counts "
+                         "(dg_grouped_gemm_fp8_ex_counts: padding rows skipped where whole waves are padding)")
     ap.add_argument("--fmt", choices=["e4m3", "e5m2"], default="e4m3",
                     help="operand FP8 format of the dense workloads 1-3 (both operands)")
     ap.add_argument("--block-rows", type=int, default=128, choices=[1, 128],
@@ -424,6 +427,9 @@ def main():
             dict(A=p.A, sA=p.sA, B=p.B, sB=p.sB).items()}
     if p.grouped:
         host["offs"] = torch.from_numpy(p.group_offsets.astype(np.int32))
+    use_counts = args.counts and p.grouped and not p.packed
+    if use_counts:
+        host["counts"] = torch.from_numpy(p.group_counts.astype(np.int32))
     copies = []
     for _ in range(R):
         d = {k: v.to(dev) for k, v in host.items()}
@@ -437,7 +443,10 @@ def main():
 
     def step(i, sh):
         d = ptrs[i % R]
-        if p.packed:
+        if use_counts:
+            st = dg.dg_grouped_gemm_fp8_ex_counts(d["A"], fa, d["sA"], p.sa_rows, d["B"], fb, d["sB"], d["C"],
+                                                  d["offs"], d["counts"], p.G, p.M, p.N, p.K, code, sh)
+        elif p.packed:
             st = dg.dg_grouped_gemm_fp8_segments(d["A"], fa, d["sA"], d["B"], fb, d["sB"], d["C"], d["offs"],
                                                  p.G, p.M, p.N, p.K, code, sh)
         elif p.grouped and plain:
@@ -496,6 +505,8 @@ def main():
            "operand_copies": R, "launch": "eager" if args.no_graph else "hip_graph"}
     if p.a_fmt != "e4m3" or p.b_fmt != "e4m3":
         cfg.update({"a_fmt": p.a_fmt, "b_fmt": p.b_fmt})
+    if use_counts:
+        cfg["padding_aware"] = True
     if p.grouped:
         cfg.update({"groups": p.G, "real_rows": p.real_rows, "active_groups": p.active_groups(),
                     "segments": "packed" if p.packed else "padded to 128 rows"})

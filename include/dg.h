@@ -217,6 +217,34 @@ int dg_grouped_gemm_fp8_ex(const void* A, int a_fmt, const float* sA, int sa_row
                            int out_dtype, hipStream_t stream);
 
 /*
+ * dg_grouped_gemm_fp8_ex for padded segments whose real row counts are
+ * known: the padding-aware form of the one-launch grouped GEMM (experts'
+ * row counts vary, FP8-for-MoE page, section 2.2; padding every segment to
+ * the 128-row tile multiplies rows that carry no token).
+ *
+ *   group_counts : DEVICE int32 [num_groups]; expert e has group_counts[e]
+ *                  real rows, rows [o_e, o_e + group_counts[e]) of its
+ *                  segment, and 0 <= group_counts[e] <= o_{e+1} - o_e.
+ *
+ * Rows [o_e + group_counts[e], o_{e+1}) are padding: their rows of C are
+ * written as zeros, whatever A and sA hold there (they need not be zeroed
+ * by the caller).  Tiles and 64-row wave sub-tiles that lie wholly in
+ * padding skip the products (a wave of padding rows still takes part in the
+ * workgroup's loads).  Real rows are computed exactly as by
+ * dg_grouped_gemm_fp8_ex; with every count equal to its segment length the
+ * result is that call's, bit for bit.  Counts outside [0, segment length]
+ * are clamped into it (DG_VALIDATE=1 rejects them with DG_ERR_INVALID_ARG);
+ * group_counts null or not 4-byte aligned -> DG_ERR_INVALID_ARG.  Everything
+ * else as for dg_grouped_gemm_fp8_ex.
+ */
+int dg_grouped_gemm_fp8_ex_counts(const void* A, int a_fmt, const float* sA, int sa_rows,
+                                  const void* B, int b_fmt, const float* sB,
+                                  void* C, const int32_t* group_offsets,
+                                  const int32_t* group_counts, int num_groups,
+                                  int64_t M_total, int64_t N, int64_t K,
+                                  int out_dtype, hipStream_t stream);
+
+/*
  * MoE grouped GEMM for few rows per expert (decode), over UNPADDED expert
  * segments, in one launch.  MoE experts share N and K while the row count
  * varies and is small at decode time (FP8-for-MoE page, section 2.2); many

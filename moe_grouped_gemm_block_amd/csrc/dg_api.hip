@@ -108,17 +108,22 @@ bool validate_offsets() {
 }
 
 // 0 = o_0 <= o_1 <= ... <= o_G = M_total, and every o_e a multiple of 128
-// when the segments are padded.
-int check_offsets(const int32_t* offs, int G, int64_t M_total, bool padded, hipStream_t stream) {
+// when the segments are padded; with real row counts, 0 <= count_e <=
+// o_{e+1} - o_e.
+int check_offsets(const int32_t* offs, int G, int64_t M_total, bool padded, hipStream_t stream,
+                  const int32_t* counts = nullptr) {
   if (!validate_offsets()) return DG_OK;
-  std::vector<int32_t> h(size_t(G) + 1);
+  std::vector<int32_t> h(size_t(G) + 1), c(counts ? size_t(G) : 0);
   if (hipMemcpyAsync(h.data(), offs, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      (counts && hipMemcpyAsync(c.data(), counts, c.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream) !=
+                     hipSuccess) ||
       hipStreamSynchronize(stream) != hipSuccess)
     return DG_ERR_LAUNCH;
   if (h[0] != 0 || int64_t(h[size_t(G)]) != M_total) return DG_ERR_INVALID_ARG;
   for (int g = 0; g < G; ++g) {
     if (h[size_t(g) + 1] < h[size_t(g)]) return DG_ERR_INVALID_ARG;
     if (padded && h[size_t(g) + 1] % dg::KBLK != 0) return DG_ERR_INVALID_ARG;
+    if (counts && (c[size_t(g)] < 0 || c[size_t(g)] > h[size_t(g) + 1] - h[size_t(g)])) return DG_ERR_INVALID_ARG;
   }
   return DG_OK;
 }
@@ -485,9 +490,12 @@ int gemm_impl(const void* A, int a_fmt, const float* sA, int sa_rows, const void
   return launch(a, out_dtype, a_fmt, b_fmt, sa_rows == 1, stream);
 }
 
+// counts: per-expert real row counts (dg_grouped_gemm_fp8_ex_counts), or
+// nullptr (every row of a segment is computed)
 int grouped_impl(const void* A, int a_fmt, const float* sA, int sa_rows, const void* B, int b_fmt,
                  const float* sB, void* C, const int32_t* group_offsets, int num_groups, int64_t M_total,
-                 int64_t N, int64_t K, int out_dtype, hipStream_t stream) {
+                 int64_t N, int64_t K, int out_dtype, hipStream_t stream, const int32_t* counts = nullptr,
+                 bool with_counts = false) {
   if (!valid_fmt(a_fmt) || !valid_fmt(b_fmt)) return DG_ERR_INVALID_ARG;
   if (sa_rows != 128 && sa_rows != 1) return DG_ERR_INVALID_ARG;
   if (num_groups < 1) return DG_ERR_INVALID_ARG;
@@ -495,9 +503,11 @@ int grouped_impl(const void* A, int a_fmt, const float* sA, int sa_rows, const v
   int st = check_common(A, sA, B, sB, C, M_total, N, K, out_dtype);
   if (st != DG_OK || M_total == 0 || N == 0) return st;
   if (group_offsets == nullptr || !aligned(group_offsets, 4)) return DG_ERR_INVALID_ARG;
-  st = check_offsets(group_offsets, num_groups, M_total, true, stream);
+  if (with_counts && (counts == nullptr || !aligned(counts, 4))) return DG_ERR_INVALID_ARG;
+  st = check_offsets(group_offsets, num_groups, M_total, true, stream, counts);
   if (st != DG_OK) return st;
   dg::GemmArgs a{};
+  a.counts = counts;
   a.A = static_cast<const uint8_t*>(A);
   a.sA = sA;
   a.B = static_cast<const uint8_t*>(B);
@@ -569,6 +579,14 @@ int dg_grouped_gemm_fp8_ex(const void* A, int a_fmt, const float* sA, int sa_row
                            int64_t M_total, int64_t N, int64_t K, int out_dtype, hipStream_t stream) {
   return grouped_impl(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, group_offsets, num_groups, M_total, N, K,
                       out_dtype, stream);
+}
+
+int dg_grouped_gemm_fp8_ex_counts(const void* A, int a_fmt, const float* sA, int sa_rows, const void* B,
+                                  int b_fmt, const float* sB, void* C, const int32_t* group_offsets,
+                                  const int32_t* group_counts, int num_groups, int64_t M_total, int64_t N,
+                                  int64_t K, int out_dtype, hipStream_t stream) {
+  return grouped_impl(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, group_offsets, num_groups, M_total, N, K,
+                      out_dtype, stream, group_counts, true);
 }
 
 int dg_quantize_fp8_blockscaled(const void* X, int in_dtype, void* Q, float* S, int64_t M, int64_t K,

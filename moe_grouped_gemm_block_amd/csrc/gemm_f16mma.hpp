@@ -187,6 +187,9 @@ struct GemmArgs {
   const float* sB;        // [G][ceil(N/128)][Kb]; Kb = ceil(K/128)
   void* C;                // [M][N]
   const int32_t* offs;    // [G+1] device, or nullptr for dense
+  // grouped, optional: [G] real rows per expert; rows [offs[e] + counts[e],
+  // offs[e+1]) are padding, written as zeros without their A rows being used
+  const int32_t* counts;
   int G;
   int M, N, K;
   int m_tiles, n_tiles;    // tiles of this launch
@@ -201,6 +204,15 @@ struct GemmArgs {
   float* ws;
   int ws_ld, ws_rows;
 };
+
+// First padding row of the segment of expert e (grouped, with per-expert
+// real row counts), else M: rows [offs[e] + counts[e], offs[e+1]) are
+// padding.  Wave-uniform.
+__device__ __forceinline__ int padding_start(const GemmArgs& p, int e) {
+  if (p.offs == nullptr || p.counts == nullptr) return p.M;
+  const int seg0 = p.offs[e], len = p.offs[e + 1] - seg0;
+  return __builtin_amdgcn_readfirstlane(seg0 + min(max(p.counts[e], 0), max(len, 0)));
+}
 
 // K-blocks [kb_begin, kb_end) of split s out of S (every split gets
 // floor or ceil of Kb / S; a split may be empty when S > Kb).
@@ -261,13 +273,17 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   const int Kb = (K + KBLK - 1) / KBLK;          // the last K-block may be partial
   const int Nb = (N + KBLK - 1) / KBLK;
   const int S = max(p.splits, 1);
-  const int kb0 = split_kb(split, S, Kb), kb1 = split_kb(split + 1, S, Kb);
+  const int kb0 = split_kb(split, S, Kb);
 
   int e = 0;
   if (p.offs != nullptr) {
     e = find_group(p.offs, p.G, m0);
     if (e >= p.G) return;                      // uniform across the workgroup
   }
+  // rows from real_end on are padding; a tile of padding rows only runs no
+  // K-blocks (its epilogue writes zeros)
+  const int real_end = padding_start(p, e);
+  const int kb1 = m0 < real_end ? split_kb(split + 1, S, Kb) : kb0;
   const int wm = (wave / NWN) * WM;            // wave sub-tile origin in the tile
   const int wn = (wave % NWN) * WN;
   // scale rows of this wave (clamped: a wave wholly past the edge stores nothing)
@@ -359,190 +375,211 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
     if (kb1 > kb0) load_row_scales(kb0);
   }
 
-  float sa_next = kb1 > kb0 && !ROW_SA ? float(sAr[kb0]) : 1.f, sb_next = kb1 > kb0 ? sBr[kb0] : 0.f;
-  for (int kb = kb0; kb < kb1; ++kb) {
-    const int stage = kSingleStage ? 0 : (kb - kb0) & 1;
-    const float s = sa_next * sb_next;         // this K-block's fp32(sA * sB)
-    float s_m[MI];                              // the factor of row group mi
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) s_m[mi] = s;
-    if constexpr (ROW_SA) {
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        s_m[mi] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (16 * mi + r16),
-                                                                         __builtin_bit_cast(int, sa_lane))) *
-                  sb_next;
-        // consumed before the next copies are issued, so that the wait for
-        // these loads cannot fall after (and drain) those copies
-        asm volatile("" : "+v"(s_m[mi]));
+  if (m0 + wm >= real_end) {
+    // A wave whose 64 rows are all padding still issues its share of every
+    // K-block's copies (they are shared by the workgroup) and passes the
+    // same waits and barriers as the others, but computes nothing: its
+    // SIMD's other wave then has the matrix core to itself.  (A separate
+    // loop: a branch inside the hot loop, or one loop body instantiated
+    // twice through a lambda, cost registers there.)
+    for (int kb = kb0; kb < kb1; ++kb) {
+      const int stage = kSingleStage ? 0 : (kb - kb0) & 1;
+      if (kb + 1 < kb1 && !kSingleStage) issue_copies(kb + 1, stage ^ 1);
+      if constexpr (kSingleStage) {
+        __syncthreads();
+        if (kb + 1 < kb1) issue_copies(kb + 1, 0);
       }
+      wait_vmem();
+      __syncthreads();
     }
-    if (kb + 1 < kb1) {
-      if constexpr (ROW_SA) load_row_scales(kb + 1);   // prefetched one K-block ahead
-      else sa_next = sAr[kb + 1];
-      sb_next = sBr[kb + 1];
-      if constexpr (!kSingleStage) issue_copies(kb + 1, stage ^ 1);
-    }
-    const uint8_t* la = lds + stage * A_BYTES;
-    const uint8_t* lb = lds + 2 * A_BYTES + stage * B_BYTES;
+  } else {
+    float sa_next = kb1 > kb0 && !ROW_SA ? float(sAr[kb0]) : 1.f, sb_next = kb1 > kb0 ? sBr[kb0] : 0.f;
+    for (int kb = kb0; kb < kb1; ++kb) {
+      const int stage = kSingleStage ? 0 : (kb - kb0) & 1;
+      const float s = sa_next * sb_next;         // this K-block's fp32(sA * sB)
+      float s_m[MI];                              // the factor of row group mi
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) s_m[mi] = s;
+      if constexpr (ROW_SA) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          s_m[mi] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (16 * mi + r16),
+                                                                           __builtin_bit_cast(int, sa_lane))) *
+                    sb_next;
+          // consumed before the next copies are issued, so that the wait for
+          // these loads cannot fall after (and drain) those copies
+          asm volatile("" : "+v"(s_m[mi]));
+        }
+      }
+      if (kb + 1 < kb1) {
+        if constexpr (ROW_SA) load_row_scales(kb + 1);   // prefetched one K-block ahead
+        else sa_next = sAr[kb + 1];
+        sb_next = sBr[kb + 1];
+        if constexpr (!kSingleStage) issue_copies(kb + 1, stage ^ 1);
+      }
+      const uint8_t* la = lds + stage * A_BYTES;
+      const uint8_t* lb = lds + 2 * A_BYTES + stage * B_BYTES;
 
-    v8h af[MI][4];
-    v8h bf[4];
-    v4f part[MI];
-    int4 y0, y1;   // raw bytes of the B column tile after the next one
-    if constexpr (!ROW_SA) {
-      // Raw FP8 fragments, all read before the first wait: A rows
-      // wm + 16 mi + r16 (the MFMA's second operand), bytes [32q, 32q+32),
-      // and the first two B column tiles.
-      int4 xa0[MI], xa1[MI];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        xa0[mi] = *reinterpret_cast<const int4*>(la + a_off0 + mi * 16 * KBLK);
-        xa1[mi] = *reinterpret_cast<const int4*>(la + a_off1 + mi * 16 * KBLK);
-      }
-      y0 = *reinterpret_cast<const int4*>(lb + b_off0);
-      y1 = *reinterpret_cast<const int4*>(lb + b_off1);
-      int4 z0 = y0, z1 = y1;
-      if (NI > 1) {
-        z0 = *reinterpret_cast<const int4*>(lb + b_off0 + 16 * KBLK);
-        z1 = *reinterpret_cast<const int4*>(lb + b_off1 + 16 * KBLK);
-      }
-      // Column tile 0, k-step by k-step: each A operand is converted just
-      // before its first MFMA, so the matrix core starts after a few
-      // conversions instead of after all of A.  The B operands of tile 1 are
-      // converted into the registers each k-step frees, and the raw bytes of
-      // tile 2 are read into those of tile 0.
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        bf[st] = fp8_operand<FB>(y0, y1, st);
+      v8h af[MI][4];
+      v8h bf[4];
+      v4f part[MI];
+      int4 y0, y1;   // raw bytes of the B column tile after the next one
+      if constexpr (!ROW_SA) {
+        // Raw FP8 fragments, all read before the first wait: A rows
+        // wm + 16 mi + r16 (the MFMA's second operand), bytes [32q, 32q+32),
+        // and the first two B column tiles.
+        int4 xa0[MI], xa1[MI];
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
-          af[mi][st] = fp8_operand<FA>(xa0[mi], xa1[mi], st);
-          part[mi] = mfma16_f16(bf[st], af[mi][st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : part[mi]);
+          xa0[mi] = *reinterpret_cast<const int4*>(la + a_off0 + mi * 16 * KBLK);
+          xa1[mi] = *reinterpret_cast<const int4*>(la + a_off1 + mi * 16 * KBLK);
         }
+        y0 = *reinterpret_cast<const int4*>(lb + b_off0);
+        y1 = *reinterpret_cast<const int4*>(lb + b_off1);
+        int4 z0 = y0, z1 = y1;
         if (NI > 1) {
-          bf[st] = fp8_operand<FB>(z0, z1, st);
-          if (NI > 2 && st == 1) y0 = *reinterpret_cast<const int4*>(lb + b_off0 + 2 * 16 * KBLK);
-          if (NI > 2 && st == 3) y1 = *reinterpret_cast<const int4*>(lb + b_off1 + 2 * 16 * KBLK);
+          z0 = *reinterpret_cast<const int4*>(lb + b_off0 + 16 * KBLK);
+          z1 = *reinterpret_cast<const int4*>(lb + b_off1 + 16 * KBLK);
         }
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * MI + (NI > 1 ? 4 : 2), 0);   // raw reads first
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                     // B operand of tile 0
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                   // A operand
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // 1 MFMA
-        }
-        if (NI > 1) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);         // B operand of tile 1
-      }
-    } else {
-      // Row-scaled A: one more live register per row group, which leaves no
-      // room for the raw fragments of both operands at once (they would be
-      // spilled, and reloading a spill inside the loop waits for the copies
-      // in flight).  A is converted first, then tile 0 runs as the others do.
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int4 x0 = *reinterpret_cast<const int4*>(la + a_off0 + mi * 16 * KBLK);
-        const int4 x1 = *reinterpret_cast<const int4*>(la + a_off1 + mi * 16 * KBLK);
-        fp8x32_to_f16<FA>(x0, x1, af[mi]);
-      }
-      y0 = *reinterpret_cast<const int4*>(lb + b_off0);
-      y1 = *reinterpret_cast<const int4*>(lb + b_off1);
-      fp8x32_to_f16<FB>(y0, y1, bf);
-      if (NI > 1) {
-        y0 = *reinterpret_cast<const int4*>(lb + b_off0 + 16 * KBLK);
-        y1 = *reinterpret_cast<const int4*>(lb + b_off1 + 16 * KBLK);
-      }
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-          part[mi] = mfma16_f16(bf[st], af[mi][st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : part[mi]);
-        if (NI > 1) {
-          bf[st] = fp8_operand<FB>(y0, y1, st);   // operand st of tile 1
-          if (NI > 2 && st == 1) y0 = *reinterpret_cast<const int4*>(lb + b_off0 + 2 * 16 * KBLK);
-          if (NI > 2 && st == 3) y1 = *reinterpret_cast<const int4*>(lb + b_off1 + 2 * 16 * KBLK);
-        }
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      if (NI > 1) {
+        // Column tile 0, k-step by k-step: each A operand is converted just
+        // before its first MFMA, so the matrix core starts after a few
+        // conversions instead of after all of A.  The B operands of tile 1 are
+        // converted into the registers each k-step frees, and the raw bytes of
+        // tile 2 are read into those of tile 0.
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-          if (st > 0) {
+          bf[st] = fp8_operand<FB>(y0, y1, st);
 #pragma unroll
-            for (int mi = 0; mi < MI; ++mi) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-              __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // 1 VALU (convert)
+          for (int mi = 0; mi < MI; ++mi) {
+            af[mi][st] = fp8_operand<FA>(xa0[mi], xa1[mi], st);
+            part[mi] = mfma16_f16(bf[st], af[mi][st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : part[mi]);
+          }
+          if (NI > 1) {
+            bf[st] = fp8_operand<FB>(z0, z1, st);
+            if (NI > 2 && st == 1) y0 = *reinterpret_cast<const int4*>(lb + b_off0 + 2 * 16 * KBLK);
+            if (NI > 2 && st == 3) y1 = *reinterpret_cast<const int4*>(lb + b_off1 + 2 * 16 * KBLK);
+          }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * MI + (NI > 1 ? 4 : 2), 0);   // raw reads first
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                     // B operand of tile 0
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi) {
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                   // A operand
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // 1 MFMA
+          }
+          if (NI > 1) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);         // B operand of tile 1
+        }
+      } else {
+        // Row-scaled A: one more live register per row group, which leaves no
+        // room for the raw fragments of both operands at once (they would be
+        // spilled, and reloading a spill inside the loop waits for the copies
+        // in flight).  A is converted first, then tile 0 runs as the others do.
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          const int4 x0 = *reinterpret_cast<const int4*>(la + a_off0 + mi * 16 * KBLK);
+          const int4 x1 = *reinterpret_cast<const int4*>(la + a_off1 + mi * 16 * KBLK);
+          fp8x32_to_f16<FA>(x0, x1, af[mi]);
+        }
+        y0 = *reinterpret_cast<const int4*>(lb + b_off0);
+        y1 = *reinterpret_cast<const int4*>(lb + b_off1);
+        fp8x32_to_f16<FB>(y0, y1, bf);
+        if (NI > 1) {
+          y0 = *reinterpret_cast<const int4*>(lb + b_off0 + 16 * KBLK);
+          y1 = *reinterpret_cast<const int4*>(lb + b_off1 + 16 * KBLK);
+        }
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi)
+            part[mi] = mfma16_f16(bf[st], af[mi][st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : part[mi]);
+          if (NI > 1) {
+            bf[st] = fp8_operand<FB>(y0, y1, st);   // operand st of tile 1
+            if (NI > 2 && st == 1) y0 = *reinterpret_cast<const int4*>(lb + b_off0 + 2 * 16 * KBLK);
+            if (NI > 2 && st == 3) y1 = *reinterpret_cast<const int4*>(lb + b_off1 + 2 * 16 * KBLK);
+          }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        if (NI > 1) {
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            if (st > 0) {
+#pragma unroll
+              for (int mi = 0; mi < MI; ++mi) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // 1 VALU (convert)
+              }
+            } else {
+              __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);     // converts of operand 0
             }
-          } else {
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);     // converts of operand 0
           }
         }
       }
-    }
-    // Column tiles 1 .. NI-1, software-pipelined: while the MFMAs of tile ni
-    // consume operand st, operand st of tile ni+1 is converted into the
-    // registers they free, and the FP32 rescale of tile ni-1 is threaded
-    // between the first MFMAs of tile ni.  Raw FP8 of tile ni+2 is read from
-    // LDS one tile ahead.
+      // Column tiles 1 .. NI-1, software-pipelined: while the MFMAs of tile ni
+      // consume operand st, operand st of tile ni+1 is converted into the
+      // registers they free, and the FP32 rescale of tile ni-1 is threaded
+      // between the first MFMAs of tile ni.  Raw FP8 of tile ni+2 is read from
+      // LDS one tile ahead.
 #pragma unroll
-    for (int ni = 1; ni < NI; ++ni) {
+      for (int ni = 1; ni < NI; ++ni) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
+        for (int st = 0; st < 4; ++st) {
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi) {
+            if (st == 0) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                acc[mi][ni - 1][r] = __builtin_fmaf(s_m[mi], part[mi][r], acc[mi][ni - 1][r]);
+            }
+            part[mi] = mfma16_f16(bf[st], af[mi][st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : part[mi]);
+          }
+          if (ni + 1 < NI) {
+            bf[st] = fp8_operand<FB>(y0, y1, st);   // operand st of tile ni+1
+            if (ni + 2 < NI && st == 1)
+              y0 = *reinterpret_cast<const int4*>(lb + b_off0 + (ni + 2) * 16 * KBLK);
+            if (ni + 2 < NI && st == 3)
+              y1 = *reinterpret_cast<const int4*>(lb + b_off1 + (ni + 2) * 16 * KBLK);
+          }
+        }
+        // pin the interleave: rescale / MFMA alternation, then MFMA / convert
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
-          if (st == 0) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              acc[mi][ni - 1][r] = __builtin_fmaf(s_m[mi], part[mi][r], acc[mi][ni - 1][r]);
-          }
-          part[mi] = mfma16_f16(bf[st], af[mi][st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : part[mi]);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU (rescale)
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
         }
         if (ni + 1 < NI) {
-          bf[st] = fp8_operand<FB>(y0, y1, st);   // operand st of tile ni+1
-          if (ni + 2 < NI && st == 1)
-            y0 = *reinterpret_cast<const int4*>(lb + b_off0 + (ni + 2) * 16 * KBLK);
-          if (ni + 2 < NI && st == 3)
-            y1 = *reinterpret_cast<const int4*>(lb + b_off1 + (ni + 2) * 16 * KBLK);
-        }
-      }
-      // pin the interleave: rescale / MFMA alternation, then MFMA / convert
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU (rescale)
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-      }
-      if (ni + 1 < NI) {
+          for (int st = 0; st < 4; ++st) {
+            if (st > 0) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          if (st > 0) {
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-              __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // 1 VALU (convert)
+              for (int mi = 0; mi < MI; ++mi) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // 1 VALU (convert)
+              }
+            } else {
+              __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);     // converts of operand 0
             }
-          } else {
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);     // converts of operand 0
           }
         }
       }
-    }
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[mi][NI - 1][r] = __builtin_fmaf(s_m[mi], part[mi][r], acc[mi][NI - 1][r]);
-    if constexpr (kSingleStage) {
-      __syncthreads();                          // every wave is done with the stage
-      if (kb + 1 < kb1) issue_copies(kb + 1, 0);
+        for (int r = 0; r < 4; ++r) acc[mi][NI - 1][r] = __builtin_fmaf(s_m[mi], part[mi][r], acc[mi][NI - 1][r]);
+      if constexpr (kSingleStage) {
+        __syncthreads();                          // every wave is done with the stage
+        if (kb + 1 < kb1) issue_copies(kb + 1, 0);
+      }
+      wait_vmem();
+      __syncthreads();
     }
-    wait_vmem();
-    __syncthreads();
   }
 
   // ---- epilogue: column tiles 2j and 2j+1 of a lane hold
-  // C[m][n0 + wn + 32 j + 8 q + 0 .. 7] ------------------------------------
+  // C[m][n0 + wn + 32 j + 8 q + 0 .. 7]; padding rows get zeros (their first
+  // row is looked up again rather than kept in a register through the loop)
+  const int pad0 = padding_start(p, p.offs != nullptr ? find_group(p.offs, p.G, m0) : 0);
   const int lane_e = lane_id();
   const int q_e = lane_e >> 4, r16_e = lane_e & 15;
   if (p.splits > 1) {
@@ -555,16 +592,15 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
     for (int mi = 0; mi < MI; ++mi) {
       const int m = m0 + wm + mi * 16 + r16_e;
       if (m >= M) continue;
+      const bool pad = m >= pad0;
       float* row = W + (size_t)(m - r0) * p.ws_ld;
 #pragma unroll
       for (int j = 0; j < NI / 2; ++j) {
         const int n = n0 + wn + 32 * j + 8 * q_e;
-        if (n < N)
-          *reinterpret_cast<float4*>(row + n) =
-              float4{acc[mi][2 * j][0], acc[mi][2 * j][1], acc[mi][2 * j][2], acc[mi][2 * j][3]};
-        if (n + 4 < N)
-          *reinterpret_cast<float4*>(row + n + 4) =
-              float4{acc[mi][2 * j + 1][0], acc[mi][2 * j + 1][1], acc[mi][2 * j + 1][2], acc[mi][2 * j + 1][3]};
+        const v4f a = pad ? v4f{0.f, 0.f, 0.f, 0.f} : acc[mi][2 * j];
+        const v4f b = pad ? v4f{0.f, 0.f, 0.f, 0.f} : acc[mi][2 * j + 1];
+        if (n < N) *reinterpret_cast<float4*>(row + n) = float4{a[0], a[1], a[2], a[3]};
+        if (n + 4 < N) *reinterpret_cast<float4*>(row + n + 4) = float4{b[0], b[1], b[2], b[3]};
       }
     }
     return;
@@ -573,13 +609,14 @@ __device__ __forceinline__ void gemm_f16mma_body(const GemmArgs& p) {
   for (int mi = 0; mi < MI; ++mi) {
     const int m = m0 + wm + mi * 16 + r16_e;
     if (m >= M) continue;
+    const bool pad = m >= pad0;
 #pragma unroll
     for (int j = 0; j < NI / 2; ++j) {
       float v[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        v[r] = acc[mi][2 * j][r];
-        v[4 + r] = acc[mi][2 * j + 1][r];
+        v[r] = pad ? 0.f : acc[mi][2 * j][r];
+        v[4 + r] = pad ? 0.f : acc[mi][2 * j + 1][r];
       }
       store_row_span<OUT_BF16, 8>(p.C, size_t(m) * N, n0 + wn + 32 * j + 8 * q_e, N, v);
     }

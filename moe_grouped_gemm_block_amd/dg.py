@@ -29,8 +29,8 @@ DG_ERR_UNSUPPORTED = -2
 DG_ERR_LAUNCH = -3
 
 EXPORTED = ("dg_gemm_fp8_blockscaled", "dg_grouped_gemm_fp8", "dg_gemm_fp8_ex", "dg_gemm_fp8_ex_noalloc",
-            "dg_grouped_gemm_fp8_ex", "dg_grouped_gemm_fp8_segments", "dg_quantize_fp8_blockscaled",
-            "dg_status_string")
+            "dg_grouped_gemm_fp8_ex", "dg_grouped_gemm_fp8_ex_counts", "dg_grouped_gemm_fp8_segments",
+            "dg_quantize_fp8_blockscaled", "dg_status_string")
 
 _lib = None
 
@@ -67,6 +67,9 @@ def lib() -> ctypes.CDLL:
         L.dg_gemm_fp8_ex_noalloc.restype = ci
         L.dg_grouped_gemm_fp8_ex.argtypes = [vp, ci, vp, ci, vp, ci, vp, vp, vp, ci, i64, i64, i64, ci, vp]
         L.dg_grouped_gemm_fp8_ex.restype = ci
+        L.dg_grouped_gemm_fp8_ex_counts.argtypes = [vp, ci, vp, ci, vp, ci, vp, vp, vp, vp, ci, i64, i64, i64,
+                                                    ci, vp]
+        L.dg_grouped_gemm_fp8_ex_counts.restype = ci
         L.dg_grouped_gemm_fp8_segments.argtypes = [vp, ci, vp, vp, ci, vp, vp, vp, ci, i64, i64, i64, ci, vp]
         L.dg_grouped_gemm_fp8_segments.restype = ci
         L.dg_quantize_fp8_blockscaled.argtypes = [vp, ci, vp, vp, i64, i64, ci, vp]
@@ -101,6 +104,12 @@ def dg_grouped_gemm_fp8_ex(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, group_offsets
                            N, K, out_dtype, stream) -> int:
     return lib().dg_grouped_gemm_fp8_ex(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, group_offsets, num_groups,
                                         M_total, N, K, out_dtype, stream)
+
+
+def dg_grouped_gemm_fp8_ex_counts(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, group_offsets, group_counts,
+                                  num_groups, M_total, N, K, out_dtype, stream) -> int:
+    return lib().dg_grouped_gemm_fp8_ex_counts(A, a_fmt, sA, sa_rows, B, b_fmt, sB, C, group_offsets,
+                                               group_counts, num_groups, M_total, N, K, out_dtype, stream)
 
 
 def dg_grouped_gemm_fp8_segments(A, a_fmt, sA, B, b_fmt, sB, C, group_offsets, num_groups, M_total, N, K,
@@ -233,8 +242,11 @@ def gemm_fp8_blockscaled(A, sA, B, sB, out_dtype="bf16", C=None, stream=None, a_
 
 
 def grouped_gemm_fp8(A, sA, B, sB, group_offsets, out_dtype="bf16", C=None, stream=None,
-                     a_fmt=None, b_fmt=None):
-    """MoE grouped GEMM over contiguous 128-row-padded expert segments."""
+                     a_fmt=None, b_fmt=None, group_counts=None):
+    """MoE grouped GEMM over contiguous 128-row-padded expert segments.
+    group_counts (device int32 [G], optional): real rows per expert; the
+    padding rows after them come out as zeros and skip the work where whole
+    wave sub-tiles are padding (dg_grouped_gemm_fp8_ex_counts)."""
     torch = _torch()
     _check_fp8(A, "A")
     _check_fp8(B, "B")
@@ -251,7 +263,14 @@ def grouped_gemm_fp8(A, sA, B, sB, group_offsets, out_dtype="bf16", C=None, stre
     code = out_code(out_dtype)
     C = _out(C, M_total, N, code, A)
     fa, fb = operand_fmt(A, a_fmt, "A"), operand_fmt(B, b_fmt, "B")
-    if fa == DG_FP8_E4M3 and fb == DG_FP8_E4M3 and rows == 128:
+    if group_counts is not None:
+        if (group_counts.dtype != torch.int32 or not group_counts.is_cuda
+                or tuple(group_counts.shape) != (G,)):
+            raise ValueError("group_counts must be a device int32 tensor of G entries")
+        st = dg_grouped_gemm_fp8_ex_counts(A.data_ptr(), fa, sA.data_ptr(), rows, B.data_ptr(), fb,
+                                           sB.data_ptr(), C.data_ptr(), group_offsets.data_ptr(),
+                                           group_counts.data_ptr(), G, M_total, N, K, code, _stream(stream))
+    elif fa == DG_FP8_E4M3 and fb == DG_FP8_E4M3 and rows == 128:
         st = dg_grouped_gemm_fp8(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(),
                                  C.data_ptr(), group_offsets.data_ptr(), G, M_total, N, K, code,
                                  _stream(stream))

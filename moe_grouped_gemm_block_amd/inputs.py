@@ -168,6 +168,7 @@ class Problem:
     b_fmt: str = "e4m3"
     sa_rows: int = BLOCK                # rows per A scale block: 128 or 1 (per token)
     packed: bool = False                # grouped segments not padded to 128 rows
+    group_counts: np.ndarray | None = None   # int32 [G]: real rows per expert (grouped)
 
     @property
     def grouped(self) -> bool:
@@ -271,7 +272,8 @@ def grouped_problem(G: int, N: int, K: int, T: int, seed: int,
     return Problem(name=name, A=qA, sA=sA, B=Bq, sB=sB, M=M_total, N=N, K=K,
                    out_dtype=out_dtype, seed=seed,
                    group_offsets=offsets.astype(np.int32),
-                   real_rows=int(counts.sum()), sa_rows=sa_rows)
+                   real_rows=int(counts.sum()), sa_rows=sa_rows,
+                   group_counts=np.asarray(counts, dtype=np.int32))
 
 
 def route(G: int, T: int, rng: np.random.Generator, popularity: str = "uniform",

@@ -211,3 +211,20 @@ def test_binding_loads_one_hip_runtime():
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=240)
     assert r.returncode == 0, r.stdout + r.stderr[-2000:]
 
+
+def test_counts_entry_point_validation(L):
+    """dg_grouped_gemm_fp8_ex_counts: a null or misaligned count array is an
+    argument error; everything else is checked as for dg_grouped_gemm_fp8_ex."""
+    def call(counts=P, **kw):
+        d = dict(A=P, sA=P, B=P, sB=P, C=P, offs=P, G=4, M=512, N=256, K=256, out=1, fa=0, fb=0, rows=128)
+        d.update(kw)
+        return dg.dg_grouped_gemm_fp8_ex_counts(d["A"], d["fa"], d["sA"], d["rows"], d["B"], d["fb"], d["sB"],
+                                                d["C"], d["offs"], counts, d["G"], d["M"], d["N"], d["K"],
+                                                d["out"], None)
+    assert call(counts=None) == INVALID
+    assert call(counts=P + 2) == INVALID
+    assert call(K=200) == UNSUP
+    assert call(G=0) == INVALID
+    assert call(M=500) == INVALID                 # M_total not a multiple of 128
+    assert call(N=0) == OK
+
