@@ -33,12 +33,20 @@ struct SkinnyJob {
   int M, N, K;
 };
 
+// Row stride (floats) of the partial sums in the final reduction: the tile's
+// 16 NI columns plus 4, so that the 16-byte stores of 8 consecutive lanes
+// (rows r .. r + 7 of one column piece) hit 8 distinct 16-byte positions of a
+// 128-byte window (rows 16 NI * 4 bytes apart would give 2 or 4 for NI = 3
+// or 1: 4- and 2-way bank conflicts).
+template <int NI>
+constexpr int skinny_red_ld() { return 16 * NI + 4; }
+
 // LDS bytes of gemm_skinny_body: per wave A in 2 stages, B in 3, row scales
 // in 2; reused for the partial sums of the final reduction.
 template <int MI, int NI, bool ROW_SA>
 constexpr int skinny_lds_bytes() {
   constexpr int wave = 2 * 16 * MI * KBLK + 3 * 16 * NI * KBLK + (ROW_SA ? 2 * 256 : 0);
-  constexpr int red = 4 * 16 * MI * 16 * NI * 4;
+  constexpr int red = 4 * 16 * MI * skinny_red_ld<NI>() * 4;
   return 4 * wave > red ? 4 * wave : red;
 }
 
@@ -194,13 +202,14 @@ __device__ __forceinline__ void gemm_skinny_body(const SkinnyJob& p, const int n
 
   // ---- fixed-order reduction of the four partial sums ----------------------
   __syncthreads();                              // every wave is done with its stages
-  float* red = reinterpret_cast<float*>(lds);   // [wave][RM][CN]
+  constexpr int LD = skinny_red_ld<NI>();
+  float* red = reinterpret_cast<float*>(lds);   // [wave][RM][LD]
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       // lane holds rows mi*16 + r16, columns ni*16 + 4q + 0..3
-      float* dst = red + (wave * RM + mi * 16 + r16) * CN + ni * 16 + 4 * q;
+      float* dst = red + (wave * RM + mi * 16 + r16) * LD + ni * 16 + 4 * q;
       *reinterpret_cast<float4*>(dst) = float4{acc[mi][ni][0], acc[mi][ni][1], acc[mi][ni][2], acc[mi][ni][3]};
     }
   __syncthreads();
@@ -214,7 +223,7 @@ __device__ __forceinline__ void gemm_skinny_body(const SkinnyJob& p, const int n
     for (int t = 0; t < 8; ++t) v[t] = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float* src = red + (w * RM + m) * CN + n8;
+      const float* src = red + (w * RM + m) * LD + n8;
       const float4 a = *reinterpret_cast<const float4*>(src);
       const float4 b = *reinterpret_cast<const float4*>(src + 4);
       v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
