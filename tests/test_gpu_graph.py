@@ -87,3 +87,33 @@ def test_dependent_chain_replays_match_eager():
         for i, (a, b) in enumerate(zip(got, want)):
             assert torch.equal(a, b), f"replay {rep}: buffer {i} differs from the eager chain"
         log(f"  replay {rep}: all {len(got)} buffers match the eager chain")
+
+
+def test_noalloc_call_captured_in_a_graph():
+    """dg_gemm_fp8_ex_noalloc captured on a stream that has never run a
+    library call (so no workspace exists for it): the split of K uses the
+    static scratch, and four replays, with eager work in between, equal the
+    eager dg_gemm_fp8_ex result bit for bit."""
+    M, N, K = 256, 4096, 4096                     # K split 4 ways
+    p = I.dense_problem(M, N, K, seed=21, out_dtype="bf16", block_log2_range=3.0)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    A, sA, B, sB = t(p.A), t(p.sA), t(p.B), t(p.sB)
+    want = dg.gemm_fp8_blockscaled(A, sA, B, sB, "bf16")
+    torch.cuda.synchronize()
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    args = (A.data_ptr(), 0, sA.data_ptr(), 128, B.data_ptr(), 0, sB.data_ptr(), C.data_ptr(), M, N, K,
+            dg.DG_OUT_BF16)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=s):
+        st = dg.dg_gemm_fp8_ex_noalloc(*args, torch.cuda.current_stream().cuda_stream)
+    assert st == dg.DG_OK, dg.dg_status_string(st)
+    for rep in range(4):
+        C.fill_(float("nan"))
+        dg.gemm_fp8_blockscaled(A, sA, B, sB, "bf16")   # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C, want), f"replay {rep} differs from the eager result"
+    log("  noalloc call captured in a graph: 4 replays equal the eager result")
+
