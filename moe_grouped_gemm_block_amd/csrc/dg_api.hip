@@ -61,9 +61,10 @@ int check_common(const void* A, const float* sA, const void* B, const float* sB,
 // included), 3256 the shared-B 256 x 256 tile for every dense problem, and
 // 8256 /
 // 4128 / 264 the 8-wave 128 x 256 / 4-wave 128 x 128 / 2-wave 128 x 64 tile
-// wherever a narrow tile is used; DG_TAIL_TILE=0 / 256 / 8256 switches off
-// the separate last round or sets its tile (256: launch_narrow's choice;
-// 8256: the 8-wave 128 x 256 tile) (tuning aids).
+// wherever a narrow tile is used; DG_TAIL_TILE=0 / 256 / 8256 / 4128 / 264
+// switches off the separate last round or sets the tile of narrow launches
+// (256: launch_narrow's choice; the others as for DG_FORCE_TILE) (tuning
+// aids).
 
 // Compute units of the current device (one workgroup of the tiled kernels
 // fills one), queried once per device and cached; 256 on the MI355X.
@@ -400,8 +401,8 @@ int launch_narrow(const dg::GemmArgs& a, const TiledSet& ks, int out_dtype, hipS
   int t = best_narrow(rows, a.N);
   if (forced_tile() == 256) t = kN256w4;
   if (forced_tile() == 8256 || tail_tile() == 8256) t = kN256w8;
-  if (forced_tile() == 4128) t = kN128w4;
-  if (forced_tile() == 264) t = kN64w2;
+  if (forced_tile() == 4128 || tail_tile() == 4128) t = kN128w4;
+  if (forced_tile() == 264 || tail_tile() == 264) t = kN64w2;
   switch (t) {
     case kN64w2: return launch_tiles(a, 64, 128, ks.k64w2[1], ks.k64w2[0], out_dtype, stream, m_tile0, m_tiles);
     case kN128w4: return launch_tiles(a, 128, 256, ks.k128w4[1], ks.k128w4[0], out_dtype, stream, m_tile0, m_tiles);

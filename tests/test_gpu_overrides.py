@@ -2,7 +2,7 @@
 every problem, 3256 = the shared-B 256 x 256 tile for every dense problem,
 8256 /
 4128 / 264 = one narrow tile wherever a narrow tile is used; DG_TAIL_TILE:
-0 = no separate last round, 8256 = the 8-wave 128 x 256 tile for it; DG_SPLITK:
+0 = no separate last round, 8256 / 4128 / 264 = that narrow tile for it; DG_SPLITK:
 1 = never split K, S = split every tiled launch S ways) give
 results inside the parity bound.  The library reads them once per process, so every setting
 runs tests/override_child.py in a child process.  Needs a GPU."""
@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 @pytest.mark.parametrize("env", [{"DG_FORCE_TILE": "512"}, {"DG_FORCE_TILE": "3256"},
                                  {"DG_FORCE_TILE": "8256"},
                                  {"DG_FORCE_TILE": "4128"}, {"DG_FORCE_TILE": "264"},
-                                 {"DG_TAIL_TILE": "8256"},
+                                 {"DG_TAIL_TILE": "8256"}, {"DG_TAIL_TILE": "4128"}, {"DG_TAIL_TILE": "264"},
                                  {"DG_FORCE_TILE": "256"}, {"DG_TAIL_TILE": "0"},
                                  {"DG_SPLITK": "1"}, {"DG_SPLITK": "3", "DG_FORCE_TILE": "4128"}],
                          ids=lambda e: "_".join(f"{k}={v}" for k, v in e.items()))
