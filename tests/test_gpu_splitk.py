@@ -109,3 +109,32 @@ def test_splitk_grouped(out):
     torch.cuda.synchronize()
     Cr, mass = oracle.grouped_gemm(qA, sA, qB, sB, offs)
     check(f"grouped 4 experts N={N} K={K} {out}", host(C), Cr, mass, out)
+
+
+def random_split_shapes(n=8, seed=17):
+    """Seeded shapes the automatic plan splits: 1-4 row tiles (M > 64, so
+    not the few-rows kernel), N up to 3000, K from 2048 to 8192 in steps of
+    16 (K-blocks >= 16, the last one often partial); each (S = min(CUs /
+    128-by-128 tiles, K-blocks / 8, 8)) >= 2 on 256 CUs."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(rng.integers(65, 513))
+        N = int(rng.integers(16, 3001))
+        K = int(rng.integers(128, 513)) * 16
+        tiles = -(-M // 128) * -(-N // 128)
+        S = min(256 // tiles, (-(-K // 128)) // 8, 8)
+        if S >= 2:
+            out.append((M, N, K, "f32" if len(out) % 2 else "bf16", S))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K,out,S", random_split_shapes())
+def test_splitk_random(M, N, K, out, S):
+    log(f"split-K random {M}x{N}x{K} {out} (S={S})")
+    p = I.dense_problem(M, N, K, seed=M + N + K, out_dtype=out, block_log2_range=3.0)
+    C = dg.gemm_fp8_blockscaled(t(p.A), t(p.sA), t(p.B), t(p.sB), out)
+    torch.cuda.synchronize()
+    Cr, mass = oracle.gemm_blockscaled(p.A, p.sA, p.B, p.sB)
+    check(f"random {M}x{N}x{K} {out} S={S}", host(C), Cr, mass, out)
+
