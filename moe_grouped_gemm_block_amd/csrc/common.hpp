@@ -43,12 +43,26 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) { return pack_bf16x2(f, 0
 // without wrapping.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+
+// 16 bytes to global memory, optionally as a non-temporal store (NT).  A
+// kernel whose workgroups all write their tiles of C at the same moment, at
+// the end of a single round, measured faster with non-temporal stores
+// (4096^3 BF16: 0.1014-0.1021 vs 0.1039-0.1043 ms; M = 64 N = 12288:
+// 15.5 vs 16.2 us); grouped and packed-segment kernels, whose stores overlap
+// other workgroups' work, were ~1 % slower with them and keep plain stores.
+template <bool NT>
+__device__ __forceinline__ void store16(void* dst, u32x4_nt w) {
+  if constexpr (NT) __builtin_nontemporal_store(w, static_cast<u32x4_nt*>(dst));
+  else *static_cast<u32x4_nt*>(dst) = w;
+}
+
 // Store the W consecutive output values v[0 .. W) of one row at columns
 // n0 .. n0 + W - 1 of C (row-major, N columns; `row_off` = row * N elements),
 // skipping columns >= N.  When every row starts 16-byte aligned (N % 8 == 0
-// for BF16, N % 4 == 0 for FP32) whole 16-byte vectors are stored; otherwise
-// element by element (a uniform branch on N).
-template <bool OUT_BF16, int W>
+// for BF16, N % 4 == 0 for FP32) whole 16-byte vectors are stored (NT: as
+// non-temporal stores); otherwise element by element (a uniform branch on N).
+template <bool OUT_BF16, int W, bool NT = false>
 __device__ __forceinline__ void store_row_span(void* C, size_t row_off, int n0, int N, const float* v) {
   constexpr int VEC = OUT_BF16 ? 8 : 4;             // elements per 16 bytes
   static_assert(W % VEC == 0, "span of whole vectors");
@@ -58,15 +72,13 @@ __device__ __forceinline__ void store_row_span(void* C, size_t row_off, int n0, 
       const int n = n0 + VEC * c;
       if (n >= N) continue;                           // whole vector in or out
       if constexpr (OUT_BF16) {
-        uint4 w;
-        w.x = pack_bf16x2(v[8 * c + 0], v[8 * c + 1]);
-        w.y = pack_bf16x2(v[8 * c + 2], v[8 * c + 3]);
-        w.z = pack_bf16x2(v[8 * c + 4], v[8 * c + 5]);
-        w.w = pack_bf16x2(v[8 * c + 6], v[8 * c + 7]);
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(C) + row_off + n) = w;
+        const u32x4_nt w = {pack_bf16x2(v[8 * c + 0], v[8 * c + 1]), pack_bf16x2(v[8 * c + 2], v[8 * c + 3]),
+                            pack_bf16x2(v[8 * c + 4], v[8 * c + 5]), pack_bf16x2(v[8 * c + 6], v[8 * c + 7])};
+        store16<NT>(static_cast<uint16_t*>(C) + row_off + n, w);
       } else {
-        *reinterpret_cast<float4*>(static_cast<float*>(C) + row_off + n) =
-            float4{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
+        const u32x4_nt w = {__builtin_bit_cast(uint32_t, v[4 * c]), __builtin_bit_cast(uint32_t, v[4 * c + 1]),
+                            __builtin_bit_cast(uint32_t, v[4 * c + 2]), __builtin_bit_cast(uint32_t, v[4 * c + 3])};
+        store16<NT>(static_cast<float*>(C) + row_off + n, w);
       }
     }
   } else {

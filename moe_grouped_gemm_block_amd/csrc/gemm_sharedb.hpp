@@ -337,7 +337,7 @@ __device__ __forceinline__ void gemm_sharedb_body(const GemmArgs& p) {
         v[r] = acc[mi][2 * j][r];
         v[4 + r] = acc[mi][2 * j + 1][r];
       }
-      store_row_span<OUT_BF16, 8>(p.C, size_t(m) * N, n0 + 32 * j + 8 * q_e, N, v);
+      store_row_span<OUT_BF16, 8, true>(p.C, size_t(m) * N, n0 + 32 * j + 8 * q_e, N, v);
     }
   }
 }

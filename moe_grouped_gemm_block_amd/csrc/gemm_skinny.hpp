@@ -53,7 +53,10 @@ constexpr int skinny_lds_bytes() {
 // The 16*NI columns from n0 of a few-rows problem, in the workgroup's LDS
 // buffer `lds` (skinny_lds_bytes bytes, 16-byte aligned).  ROW_SA: sA holds
 // one scale per row and K-block ([M][Kb]).
-template <int MI, int NI, bool OUT_BF16, int FA = FMT_E4M3, int FB = FMT_E4M3, bool ROW_SA = false>
+// NT_C: C is written with non-temporal stores (the dense few-rows kernel,
+// whose workgroups all store at the end of its single round).
+template <int MI, int NI, bool OUT_BF16, int FA = FMT_E4M3, int FB = FMT_E4M3, bool ROW_SA = false,
+          bool NT_C = false>
 __device__ __forceinline__ void gemm_skinny_body(const SkinnyJob& p, const int n0, uint8_t* lds) {
   constexpr int NW = 4;                         // waves, each a quarter of the K-blocks
   constexpr int RM = 16 * MI, CN = 16 * NI;     // rows / columns of the workgroup tile
@@ -229,7 +232,7 @@ __device__ __forceinline__ void gemm_skinny_body(const SkinnyJob& p, const int n
       v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
       v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
     }
-    store_row_span<OUT_BF16, 8>(p.C, size_t(m) * N, n, N, v);
+    store_row_span<OUT_BF16, 8, NT_C>(p.C, size_t(m) * N, n, N, v);
   }
 }
 
@@ -237,7 +240,7 @@ template <int MI, int NI, bool OUT_BF16, int FA, int FB, bool ROW_SA>
 __device__ __forceinline__ void gemm_skinny_dense(const GemmArgs& p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[skinny_lds_bytes<MI, NI, ROW_SA>()];
   const SkinnyJob j{p.A, p.sA, p.B, p.sB, p.C, p.M, p.N, p.K};
-  gemm_skinny_body<MI, NI, OUT_BF16, FA, FB, ROW_SA>(j, int(blockIdx.x) * 16 * NI, lds);
+  gemm_skinny_body<MI, NI, OUT_BF16, FA, FB, ROW_SA, true>(j, int(blockIdx.x) * 16 * NI, lds);
 }
 
 // Grouped GEMM over unpadded expert segments (rows [o_e, o_{e+1}) of A and C
