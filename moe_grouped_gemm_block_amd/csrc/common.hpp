@@ -57,6 +57,12 @@ __device__ __forceinline__ void store16(void* dst, u32x4_nt w) {
   else *static_cast<u32x4_nt*>(dst) = w;
 }
 
+// 16 bytes from global memory with a non-temporal load (data read once).
+__device__ __forceinline__ uint4 load16_nt(const void* src) {
+  const u32x4_nt w = __builtin_nontemporal_load(static_cast<const u32x4_nt*>(src));
+  return uint4{w.x, w.y, w.z, w.w};
+}
+
 // Store the W consecutive output values v[0 .. W) of one row at columns
 // n0 .. n0 + W - 1 of C (row-major, N columns; `row_off` = row * N elements),
 // skipping columns >= N.  When every row starts 16-byte aligned (N % 8 == 0

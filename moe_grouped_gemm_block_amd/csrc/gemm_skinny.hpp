@@ -12,8 +12,9 @@
 //   * every wave copies its own K-blocks (all 16*MI rows of A, 16*NI rows of
 //     B) straight into a private LDS region with bounds-checked buffer->LDS
 //     loads and waits for them with its own vmcnt.  B, the bytes that come
-//     from HBM, runs two K-blocks ahead (three stages); A, which every
-//     workgroup re-reads from L2, runs one ahead (two stages);
+//     from HBM, runs two K-blocks ahead (three stages) and is copied with the
+//     non-temporal cache policy (read once); A, which every workgroup
+//     re-reads from L2, runs one ahead (two stages);
 //   * the four per-wave partial sums are added through LDS in a fixed order
 //     (wave 0 + 1 + 2 + 3) before the single rounding to BF16 / FP32, so the
 //     result is bitwise repeatable.
@@ -120,7 +121,7 @@ __device__ __forceinline__ void gemm_skinny_body(const SkinnyJob& p, const int n
     const uint32_t base = lds_wave + uint32_t(2 * A_BYTES + stage * B_BYTES);
 #pragma unroll
     for (int c = 0; c < B_CH; ++c)
-      copy16_to_lds(rB, ((c & 1) ? od : ev) + uint32_t(8 * c * K), base + uint32_t(c * 1024));
+      copy16_to_lds_nt(rB, ((c & 1) ? od : ev) + uint32_t(8 * c * K), base + uint32_t(c * 1024));
   };
 
   v4f acc[MI][NI];

@@ -28,13 +28,16 @@
 // rounding through 53 bits is innocuous for one division of 24-bit numbers).
 //
 // Memory-bound: each element is read once (2 or 4 bytes) and written once
-// (1 byte).  The encoder above takes about 20 instructions per element; the
-// kernels use it only as the fallback of a cheaper one (fast_codes4 below).
+// (1 byte), both with non-temporal loads and stores (4096 x 4096 BF16, 1 x 128
+// blocks: 15.3 -> 14.0 us; 128 x 128: 16.9 -> 16.4 us).  The encoder above
+// takes about 20 instructions per element; the kernels use it only as the
+// fallback of a cheaper one (fast_codes4 below).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.hpp"
 #include "kernels.hpp"
 
 namespace dg {
@@ -197,7 +200,7 @@ __device__ __forceinline__ void q1_load(Q1Buf<IN_BF16>& b, const QuantArgs& p, l
     const uint4* src = IN_BF16 ? reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.X) + e0)
                                : reinterpret_cast<const uint4*>(static_cast<const float*>(p.X) + e0);
 #pragma unroll
-    for (int i = 0; i < N; ++i) b.w[i] = src[i];
+    for (int i = 0; i < N; ++i) b.w[i] = load16_nt(src + i);
   } else {
 #pragma unroll
     for (int i = 0; i < N; ++i) b.w[i] = uint4{0u, 0u, 0u, 0u};   // joins the reduction
@@ -228,7 +231,7 @@ __device__ __forceinline__ void q1_process(const Q1Buf<IN_BF16>& b, const QuantA
         w[j] = exact_codes4(q1_value(b, 4 * j), q1_value(b, 4 * j + 1), q1_value(b, 4 * j + 2),
                             q1_value(b, 4 * j + 3), sn);
     }
-    *reinterpret_cast<uint4*>(p.Q + size_t(blk) * 128 + size_t(lane & 7) * 16) = uint4{w[0], w[1], w[2], w[3]};
+    store16<true>(p.Q + size_t(blk) * 128 + size_t(lane & 7) * 16, u32x4_nt{w[0], w[1], w[2], w[3]});
     if ((lane & 7) == 0) p.S[blk] = s;
   }
 }
@@ -265,7 +268,7 @@ __device__ __forceinline__ void quant128_body(const QuantArgs& p) {
     const uint4* src = IN_BF16 ? reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.X) + e0)
                                : reinterpret_cast<const uint4*>(static_cast<const float*>(p.X) + e0);
 #pragma unroll
-    for (int i = 0; i < N; ++i) b.w[i] = src[i];
+    for (int i = 0; i < N; ++i) b.w[i] = load16_nt(src + i);
   } else {
 #pragma unroll
     for (int i = 0; i < N; ++i) b.w[i] = uint4{0u, 0u, 0u, 0u};
@@ -295,7 +298,7 @@ __device__ __forceinline__ void quant128_body(const QuantArgs& p) {
         w[j] = exact_codes4(q1_value(b, 4 * j), q1_value(b, 4 * j + 1), q1_value(b, 4 * j + 2),
                             q1_value(b, 4 * j + 3), sn);
     }
-    *reinterpret_cast<uint4*>(p.Q + e0) = uint4{w[0], w[1], w[2], w[3]};
+    store16<true>(p.Q + e0, u32x4_nt{w[0], w[1], w[2], w[3]});
   }
   if (t == 0) p.S[size_t(rb) * Kb + kb] = s;
 }
