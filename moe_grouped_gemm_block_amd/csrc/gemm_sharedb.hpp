@@ -26,8 +26,11 @@
 //   * two FP16 stages (128 KB of LDS): while the MFMAs of K-block kb read
 //     stage kb % 2, the waves convert K-block kb + 1 into the other stage;
 //     the operands of K-block kb + 1 (A) and kb + 2 (B) are loaded into
-//     registers at the top of K-block kb, a whole K-block ahead of their
-//     use.  One barrier per K-block.  Every load is an ordinary,
+//     registers early in K-block kb, a whole K-block ahead of their use.
+//     One barrier per K-block, placed before its last column tile: that
+//     tile's MFMAs then overlap the reads of the next K-block's first B
+//     operands and the conversion of its A, so a new K-block starts with
+//     its operands in registers.  Every load is an ordinary,
 //     compiler-visible buffer load, so the compiler counts its waits;
 //   * the FP16 rows are 256 bytes (16 granules of 16 bytes); granule g of
 //     row r sits at g ^ swzb(r % 16), which makes the operand reads free of
@@ -220,19 +223,49 @@ __device__ __forceinline__ void gemm_sharedb_body(const GemmArgs& p) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // ---- prologue: B(0) -> stage 0; A(0), B(1) in flight -----------------------
+  // Operands of the K-block about to start: A converted, B of column tile 0
+  // read from its stage.  Both are prepared during the last column tile of
+  // the K-block before (prologue for K-block 0), so that the MFMAs of a new
+  // K-block can issue right away.
+  v8h af[MI][4];
+  v8h bf[4];
+  auto convert_a = [&](int st) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+      af[mi][st] = fp8_operand<FA>(__builtin_bit_cast(int4, araw[mi][0]), __builtin_bit_cast(int4, araw[mi][1]), st);
+  };
+
+  // ---- prologue: B(0) -> stage 0; A(0) converted; B(1) in flight -----------
   if (Kb > 0) {
     load_b(0);
+    load_a(0);
 #pragma unroll
     for (int c = 0; c < 4; ++c) convert_b(c, 0);
-    load_a(0);
     load_b(1);
     if constexpr (ROW_SA) load_row_scales(0);
   }
   __syncthreads();
+  if (Kb > 0) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      convert_a(st);
+      bf[st] = read_b(0, 0, st);
+    }
+  }
 
   float sa_next = Kb > 0 && !ROW_SA ? float(sAr[0]) : 1.f;
   float sb0_next = Kb > 0 ? sB0[0] : 0.f, sb1_next = Kb > 0 ? sB1[0] : 0.f;
+  // Partials of column tiles ni (part[ni & 1]); the partial of the last
+  // column tile is rescaled during column tile 0 of the next K-block, with
+  // the factors of its own K-block (s_last; zero before the first K-block).
+  // With per-row A scales the two extra live factors would not fit the
+  // register budget: there the last tile is rescaled at the end of its
+  // K-block.
+  constexpr bool kDeferLast = !ROW_SA;
+  v4f part[2][MI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) part[1][mi] = v4f{0.f, 0.f, 0.f, 0.f};
+  float s_last[MI] = {0.f, 0.f};
   for (int kb = 0; kb < Kb; ++kb) {
     const int stage = kSingleStage ? 0 : kb & 1;
     // this K-block's factors: [mi][column half]
@@ -241,7 +274,7 @@ __device__ __forceinline__ void gemm_sharedb_body(const GemmArgs& p) {
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         s[mi][0] = sa_row[mi] * sb0_next;
-        s[mi][1] = sa_row[mi] * sb1_next;
+        s[mi][1] = 0.f;                          // set at column tile NI / 2
       }
     } else {
       const float s0 = sa_next * sb0_next, s1 = sa_next * sb1_next;
@@ -251,6 +284,7 @@ __device__ __forceinline__ void gemm_sharedb_body(const GemmArgs& p) {
         s[mi][1] = s1;
       }
     }
+    const float sb1_cur = sb1_next;
     {
       const int kn = min(kb + 1, Kb - 1);        // stays in bounds at the last K-block
       if constexpr (!ROW_SA) sa_next = sAr[kn];
@@ -260,46 +294,56 @@ __device__ __forceinline__ void gemm_sharedb_body(const GemmArgs& p) {
 
     // Column tile ni, k-step st: 2 MFMAs (row tiles mi = 0, 1) per B
     // operand; the B operands of tile ni + 1 are read into the registers the
-    // MFMAs free, and the rescale of tile ni - 1 runs between the MFMAs of
-    // tile ni.  Inside tile 0, A(kb) is converted k-step by k-step just
-    // before its MFMAs; tile 1 issues the loads of A(kb + 1); tiles 1-4
-    // convert B(kb + 1) into the other stage (read by every wave during
-    // K-block kb - 1, which the barrier at its end has closed; past the last
-    // K-block this writes zeros into a stage nobody reads); tile 4 issues
-    // the loads of B(kb + 2).  Scheduling barriers between the tiles keep
-    // this order.
-    v8h af[MI][4];
-    v8h bf[4];
-#pragma unroll
-    for (int st = 0; st < 4; ++st) bf[st] = read_b(stage, 0, st);
-    v4f part[2][MI];
+    // MFMAs free, and the rescale of tile ni - 1 (for tile 0: the last tile
+    // of the previous K-block) runs between the MFMAs of tile ni.  Tile 0
+    // issues the loads of A(kb + 1) (its registers were freed by the
+    // conversion of A(kb)); tiles 1-4 convert B(kb + 1) into the other stage
+    // (read by every wave during K-block kb - 1, which the barrier before
+    // its last tile has closed; past the last K-block this writes zeros into
+    // a stage nobody reads); tile 4 issues the loads of B(kb + 2).  The one
+    // barrier of the K-block sits before tile 15: by then every wave has
+    // read its last operands from this K-block's stage and written its part
+    // of the next.  Tile 15 then reads the next K-block's tile-0 operands
+    // from the other stage and converts A(kb + 1), k-step by k-step, into
+    // the registers its own MFMAs free.  Scheduling barriers between the
+    // tiles keep this order.
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       v4f* pc = part[ni & 1];
-      if (ni == 1) {
-        load_a(kb + 1);
-        if constexpr (ROW_SA) load_row_scales(min(kb + 1, Kb - 1));
+      if (ni == NI - 1) {
+        if constexpr (!kSingleStage) __syncthreads();
       }
+      if (ni == 0) load_a(kb + 1);
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        if (ni == 0) {
-#pragma unroll
-          for (int mi = 0; mi < MI; ++mi)
-            af[mi][st] = fp8_operand<FA>(__builtin_bit_cast(int4, araw[mi][0]),
-                                         __builtin_bit_cast(int4, araw[mi][1]), st);
-        }
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
           pc[mi] = mfma16_f16(bf[st], af[mi][st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : pc[mi]);
-        if (ni + 1 < NI) bf[st] = read_b(stage, ni + 1, st);
+        if (ni + 1 < NI) {
+          bf[st] = read_b(stage, ni + 1, st);
+        } else {
+          convert_a(st);
+          if constexpr (!kSingleStage) bf[st] = read_b(stage ^ 1, 0, st);
+        }
       }
-      if (ni > 0) {
+      if (ni > 0 || kDeferLast) {
         const v4f* pp = part[(ni - 1) & 1];
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
+        for (int mi = 0; mi < MI; ++mi) {
+          const float f = ni == 0 ? s_last[mi] : s[mi][(ni - 1) >= NI / 2];
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            acc[mi][ni - 1][r] = __builtin_fmaf(s[mi][(ni - 1) >= NI / 2], pp[mi][r], acc[mi][ni - 1][r]);
+            acc[mi][(ni + NI - 1) % NI][r] = __builtin_fmaf(f, pp[mi][r], acc[mi][(ni + NI - 1) % NI][r]);
+        }
+      }
+      if constexpr (ROW_SA) {
+        // per-row factors of the second column half, then the next
+        // K-block's row scales into the registers they came from
+        if (ni == NI / 2) {
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi) s[mi][1] = sa_row[mi] * sb1_cur;
+          load_row_scales(min(kb + 1, Kb - 1));
+        }
       }
       if constexpr (!kSingleStage) {
         if (ni >= 1 && ni <= 4) convert_b(ni - 1, stage ^ 1);
@@ -308,17 +352,31 @@ __device__ __forceinline__ void gemm_sharedb_body(const GemmArgs& p) {
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < MI; ++mi) {
+      if constexpr (kDeferLast) {
+        s_last[mi] = s[mi][1];
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        acc[mi][NI - 1][r] = __builtin_fmaf(s[mi][1], part[(NI - 1) & 1][mi][r], acc[mi][NI - 1][r]);
+        for (int r = 0; r < 4; ++r)
+          acc[mi][NI - 1][r] = __builtin_fmaf(s[mi][1], part[1][mi][r], acc[mi][NI - 1][r]);
+      }
+    }
     if constexpr (kSingleStage) {
       __syncthreads();                          // every wave is done with the stage
 #pragma unroll
       for (int c = 0; c < 4; ++c) convert_b(c, 0);
       load_b(kb + 2);
+      __syncthreads();
+#pragma unroll
+      for (int st = 0; st < 4; ++st) bf[st] = read_b(0, 0, st);
     }
-    __syncthreads();
+  }
+  if constexpr (kDeferLast) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc[mi][NI - 1][r] = __builtin_fmaf(s_last[mi], part[1][mi][r], acc[mi][NI - 1][r]);
   }
 
   // ---- epilogue: column tiles 2j and 2j+1 of a lane hold
