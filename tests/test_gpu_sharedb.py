@@ -57,10 +57,12 @@ def check(p, what):
 
 
 # M, N, K, out: 16 x 16 and 8 x 32 tiles of 256 x 256; K = 272 and 400 end in
-# a partial K-block; N = 4080 (last tile 240 columns, rows of C 16-byte
-# aligned) and N = 4090 (element-wise stores)
+# a partial K-block, K = 16 and 112 are one partial K-block, K = 128 one full
+# one; N = 4080 (last tile 240 columns, rows of C 16-byte aligned) and
+# N = 4090 (element-wise stores)
 SHAPES = [(4096, 4096, 128, "f32"), (4096, 4096, 272, "bf16"), (4096, 4080, 384, "f32"),
-          (4096, 4090, 256, "f32"), (4096, 4090, 144, "bf16"), (2048, 8192, 400, "f32")]
+          (4096, 4090, 256, "f32"), (4096, 4090, 144, "bf16"), (2048, 8192, 400, "f32"),
+          (4096, 4096, 16, "f32"), (4096, 4096, 112, "bf16")]
 
 
 @pytest.mark.parametrize("M,N,K,out", SHAPES)
@@ -79,11 +81,10 @@ def test_sharedb_formats(a_fmt, b_fmt):
     check(p, f"{a_fmt}x{b_fmt} {M}x{N}x{K} f32")
 
 
-@pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_sharedb_row_scales(out):
+@pytest.mark.parametrize("out,K", [("f32", 400), ("bf16", 400), ("f32", 112), ("bf16", 640)])
+def test_sharedb_row_scales(out, K):
     M = N = 4096
-    K = 400
-    log(f"shared-B per-row A scales {out}")
+    log(f"shared-B per-row A scales {out} K={K}")
     p = I.dense_problem(M, N, K, seed=11, out_dtype=out, block_log2_range=3.0, sa_rows=1)
     check(p, f"1x128 A scales {M}x{N}x{K} {out}")
 
