@@ -295,7 +295,8 @@ __device__ __forceinline__ void gemm_sharedb_body(const GemmArgs& p) {
     // Column tile ni, k-step st: 2 MFMAs (row tiles mi = 0, 1) per B
     // operand; the B operands of tile ni + 1 are read into the registers the
     // MFMAs free, and the rescale of tile ni - 1 (for tile 0: the last tile
-    // of the previous K-block) runs between the MFMAs of tile ni.  Tile 0
+    // of the previous K-block; with per-row A scales that one is rescaled at
+    // the end of its own K-block) runs between the MFMAs of tile ni.  Tile 0
     // issues the loads of A(kb + 1) (its registers were freed by the
     // conversion of A(kb)); tiles 1-4 convert B(kb + 1) into the other stage
     // (read by every wave during K-block kb - 1, which the barrier before
