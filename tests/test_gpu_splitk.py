@@ -138,3 +138,33 @@ def test_splitk_random(M, N, K, out, S):
     Cr, mass = oracle.gemm_blockscaled(p.A, p.sA, p.B, p.sB)
     check(f"random {M}x{N}x{K} {out} S={S}", host(C), Cr, mass, out)
 
+
+
+def test_splitk_concurrent_streams():
+    """Split-K calls on three streams at once, four rounds without a
+    synchronisation in between.  Each stream has its own workspace, so every
+    result equals the same call run alone bit for bit, and the oracle within
+    the bound."""
+    shapes = [(256, 4096, 4096, "bf16"), (128, 2048, 4096, "f32"), (136, 1000, 2048, "bf16")]
+    probs = [I.dense_problem(M, N, K, seed=40 + i, out_dtype=out, block_log2_range=3.0)
+             for i, (M, N, K, out) in enumerate(shapes)]
+    dev = [(t(p.A), t(p.sA), t(p.B), t(p.sB)) for p in probs]
+    alone = []
+    for p, d in zip(probs, dev):
+        C = dg.gemm_fp8_blockscaled(*d, p.out_dtype)
+        torch.cuda.synchronize()
+        alone.append(host(C))
+    streams = [torch.cuda.Stream() for _ in probs]
+    outs = [[] for _ in probs]
+    torch.cuda.synchronize()
+    for _ in range(4):
+        for i, (p, d, s) in enumerate(zip(probs, dev, streams)):
+            with torch.cuda.stream(s):
+                outs[i].append(dg.gemm_fp8_blockscaled(*d, p.out_dtype, stream=s))
+    torch.cuda.synchronize()
+    for i, p in enumerate(probs):
+        log(f"split-K stream {i}: {p.M}x{p.N}x{p.K} {p.out_dtype}")
+        for C in outs[i]:
+            assert np.array_equal(host(C), alone[i]), f"stream {i}: result differs from the call alone"
+        Cr, mass = oracle.gemm_blockscaled(p.A, p.sA, p.B, p.sB)
+        check(f"stream {i} {p.M}x{p.N}x{p.K}", alone[i], Cr, mass, p.out_dtype)
