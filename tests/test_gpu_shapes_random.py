@@ -1,6 +1,7 @@
 """Seeded random dense and grouped shapes through the automatic tile choice (the host picks
 among seven tile shapes from M, N and the CU count, and may split a grid
-into a main launch and a last-round launch), each compared with the CPU
+into a main launch and a last-round launch; six dense cases are sized for the
+shared-B 256 x 256 tile), each compared with the CPU
 oracle to the parity bound.  Rows are sampled for the larger shapes, always
 including the first and last rows of every 128-row tile.  Needs a GPU."""
 import sys
@@ -36,6 +37,12 @@ def cases(n=24, seed=2024):
     # a last round of 1 .. 4 row tiles)
     out += [(2048, 4096, 256, "bf16"), (33 * 128, 2048, 128, "bf16"), (36 * 128 - 5, 1000, 144, "f32"),
             (1536, 4104, 128, "bf16")]
+    # dense shapes that take the shared-B 256 x 256 tile (M a multiple of 256,
+    # whole rounds of 256 tiles on 256 CUs) with ragged N and random K
+    for M, n_tiles in ((4096, 16), (2048, 32), (8192, 8), (1024, 64), (4096, 32), (512, 128)):
+        N = 256 * n_tiles - int(rng.integers(0, 256))
+        K = int(16 * rng.integers(1, 40))
+        out.append((M, N, K, "bf16" if rng.random() < 0.5 else "f32"))
     return out
 
 
